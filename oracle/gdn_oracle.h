@@ -1,0 +1,72 @@
+/*
+ * gdn_oracle.h -- plain fp64 CPU oracle for the gated delta rule.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this library: it exists so that tests, the smoke check and the CPU
+ * baseline leg of the benchmark can compare the HIP kernels against an
+ * obviously correct definition.  It shares no code, header, table or helper
+ * with the HIP library.
+ *
+ * What it follows (pages cited by title and section):
+ *  - "Qwen3.5 Gated Delta Net NKI Kernel for AWS Neuron" (Hugging Face model
+ *    card), section "How It Works": the per-token recurrence
+ *      decay the state by exp(log g); read a = S^T k; delta = beta (v - a);
+ *      write S += k delta^T; output o = S^T q from the updated state.
+ *  - same card, section "Correctness Contract": log g <= 0 in Qwen models
+ *    (no clamping is applied here either); each (batch, head) is independent.
+ *  - "Qwen3.6: Fused DeltaNet Direct-Solve Follow-Up" (comment on the PR
+ *    "Add Qwen3.6-27B hybrid DeltaNet/GQA contrib model and vLLM serving
+ *    path"), sections "Why This Exists" and "Implementation Details": the
+ *    chunked form solves the lower-triangular causal system directly
+ *    (forward substitution on the right-hand side) instead of the Neumann
+ *    power-doubling series.  Both solves are exposed here so that their
+ *    equivalence in exact-ish arithmetic can be pinned.
+ *
+ * Layouts (all row-major, innermost dimension last, fp64, host memory):
+ *   q, k   [B, T, Hk, dk]
+ *   v      [B, T, Hv, dv]
+ *   log_g  [B, T, Hv]        (natural-log decay, g = exp(log_g))
+ *   beta   [B, T, Hv]
+ *   h0, hT [B, Hv, dk, dv]   (h0 may be NULL = zero state; hT may be NULL)
+ *   o      [B, T, Hv, dv]
+ * Value head h reads key head h / (Hv / Hk) (contiguous grouping).
+ * q/k normalisation when qk_l2norm != 0:  x / max(||x||_2, 1e-6).
+ * Every routine returns 0 on success and a negative number on bad arguments.
+ */
+#ifndef GDN_ORACLE_H
+#define GDN_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Token-serial definition, threaded over independent (b, h) pairs. */
+int oracle_gdn_sequential(int B, int T, int Hk, int Hv, int dk, int dv,
+                          int qk_l2norm, double q_scale,
+                          const double* q, const double* k, const double* v,
+                          const double* log_g, const double* beta,
+                          const double* h0, double* o, double* hT,
+                          int nthreads);
+
+/* Chunk-parallel (WY) form with a direct forward-substitution solve of the
+ * unit lower-triangular chunk system.  Must agree with the sequential form
+ * up to rounding; used only to pin that equivalence. */
+int oracle_gdn_chunked(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                       int qk_l2norm, double q_scale,
+                       const double* q, const double* k, const double* v,
+                       const double* log_g, const double* beta,
+                       const double* h0, double* o, double* hT);
+
+/* (I + A)^-1 for strictly lower-triangular A (n x n, row-major) by forward
+ * substitution.  Entries of A on or above the diagonal are ignored. */
+int oracle_unit_lower_inverse(int n, const double* A, double* Tinv);
+
+/* The same inverse by Neumann power doubling: prod_j (I + (-A)^(2^j)),
+ * j = 0 .. ceil(log2 n) - 1.  Exact in real arithmetic because A is
+ * nilpotent; kept only to pin the equivalence the pages rely on. */
+int oracle_neumann_inverse(int n, const double* A, double* Tinv);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,327 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function takes an oracle library handle and raises
+AssertionError when the oracle disagrees with:
+  * the expanded matrix form of the recurrence, S_t = g_t (I - b_t k_t k_t^T)
+    S_{t-1} + b_t k_t v_t^T, o_t = S_t^T q_t (evaluated here with numpy
+    matrices, a different expression from the oracle's five-step loop);
+  * closed forms (no write when beta = 0; exact overwrite with orthonormal
+    keys; the scalar recurrence at d = 1; a small exact example);
+  * invariants (identity plumbing, unit-key read-back, split invariance,
+    linearity, non-expansiveness, GQA grouping, normalisation scale
+    invariance);
+  * library routines (numpy's matrix inverse for the triangular solve).
+
+The same list is run against deliberately broken builds of the oracle
+(tests/test_oracle_mutants.py) to show that each plausible mistake is caught.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _inputs(rng, B, T, Hk, Hv, dk, dv, gate="uniform"):
+    q = rng.standard_normal((B, T, Hk, dk))
+    k = rng.standard_normal((B, T, Hk, dk))
+    v = rng.standard_normal((B, T, Hv, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, Hv))))
+    if gate == "uniform":
+        log_g = rng.uniform(-0.5, -0.01, size=(B, T, Hv))
+    else:  # Qwen-scale gates: -exp(A_log) softplus(dt)
+        a_log = rng.uniform(-2.0, 1.0, size=(Hv,))
+        log_g = -np.exp(a_log) * np.logaddexp(0.0, rng.standard_normal((B, T, Hv)))
+    h0 = 0.02 * rng.standard_normal((B, Hv, dk, dv))
+    return q, k, v, log_g, beta, h0
+
+
+def _unit(x):
+    n = np.linalg.norm(x, axis=-1, keepdims=True)
+    return x / np.maximum(n, 1e-6)
+
+
+def _rel(a, b):
+    den = max(np.linalg.norm(b), 1e-300)
+    return np.linalg.norm(a - b) / den
+
+
+# --------------------------------------------------------------------------
+
+
+def pin_identity_plumbing(lib):
+    """beta = 0, g = 1: state untouched (bitwise), o_t = S0^T q_hat_t."""
+    rng = _rng(1)
+    B, T, Hk, Hv, d = 2, 9, 2, 4, 6
+    q, k, v, _, _, h0 = _inputs(rng, B, T, Hk, Hv, d, d)
+    log_g = np.zeros((B, T, Hv))
+    beta = np.zeros((B, T, Hv))
+    o, hT = oracle.gdn_sequential(q, k, v, log_g, beta, h0, lib=lib)
+    assert np.array_equal(hT, h0), "state changed although beta=0 and g=1"
+    qh = _unit(q)
+    r = Hv // Hk
+    for h in range(Hv):
+        exp_o = np.einsum("btk,bkv->btv", qh[:, :, h // r, :], h0[:, h])
+        assert _rel(o[:, :, h], exp_o) < 1e-13
+
+
+def pin_matrix_form(lib):
+    """Oracle equals the expanded matrix recurrence (numpy), several shapes."""
+    for seed, (B, T, Hk, Hv, dk, dv, qs, gate) in enumerate([
+            (1, 17, 1, 1, 5, 5, 1.0, "uniform"),
+            (2, 11, 2, 4, 4, 4, 0.75, "qwen"),
+            (1, 13, 1, 3, 3, 7, 1.0, "uniform"),
+            (1, 9, 2, 2, 6, 3, 1.25, "qwen")]):
+        rng = _rng(100 + seed)
+        q, k, v, log_g, beta, h0 = _inputs(rng, B, T, Hk, Hv, dk, dv, gate)
+        o, hT = oracle.gdn_sequential(q, k, v, log_g, beta, h0, q_scale=qs, lib=lib)
+        qh, kh = _unit(q), _unit(k)
+        r = Hv // Hk
+        I = np.eye(dk)
+        for b in range(B):
+            for h in range(Hv):
+                S = h0[b, h].copy()
+                for t in range(T):
+                    kk = kh[b, t, h // r][:, None]
+                    g = np.exp(log_g[b, t, h])
+                    bt = beta[b, t, h]
+                    S = g * (I - bt * kk @ kk.T) @ S + bt * kk @ v[b, t, h][None, :]
+                    exp_o = qs * (S.T @ qh[b, t, h // r])
+                    assert _rel(o[b, t, h], exp_o) < 1e-12, (seed, b, h, t)
+                assert _rel(hT[b, h], S) < 1e-12, (seed, b, h)
+
+
+def pin_unit_key_readback(lib):
+    """g = 1, beta = 1, unit k: S_t^T k_t = v_t (read with q_t = k_t)."""
+    rng = _rng(2)
+    B, T, H, d = 1, 12, 2, 8
+    _, _, v, _, _, h0 = _inputs(rng, B, T, H, H, d, d)
+    # basis keys, normalisation off
+    idx = rng.integers(0, d, size=(B, T, H))
+    k = np.zeros((B, T, H, d))
+    for t in range(T):
+        for h in range(H):
+            k[0, t, h, idx[0, t, h]] = 1.0
+    ones = np.ones((B, T, H))
+    o, _ = oracle.gdn_sequential(k, k, v, np.zeros((B, T, H)), ones, h0,
+                                 qk_l2norm=False, lib=lib)
+    assert np.max(np.abs(o - v)) < 1e-14 * max(1.0, np.max(np.abs(v)))
+    # random unit keys, normalisation on
+    k = _unit(rng.standard_normal((B, T, H, d)))
+    o, _ = oracle.gdn_sequential(k, k, v, np.zeros((B, T, H)), ones, h0, lib=lib)
+    assert np.max(np.abs(o - v)) < 1e-12
+
+
+def pin_no_write_closed_form(lib):
+    """beta = 0: o_t = exp(sum_{s<=t} log g_s) S0^T q_hat_t."""
+    rng = _rng(3)
+    B, T, Hk, Hv, d = 1, 20, 1, 2, 5
+    q, k, v, log_g, _, h0 = _inputs(rng, B, T, Hk, Hv, d, d, "qwen")
+    beta = np.zeros((B, T, Hv))
+    o, hT = oracle.gdn_sequential(q, k, v, log_g, beta, h0, lib=lib)
+    qh = _unit(q)
+    for h in range(Hv):
+        G = np.exp(np.cumsum(log_g[0, :, h]))
+        exp_o = G[:, None] * (qh[0, :, 0] @ h0[0, h])
+        assert _rel(o[0, :, h], exp_o) < 1e-13
+        assert _rel(hT[0, h], G[-1] * h0[0, h]) < 1e-13
+
+
+def pin_orthonormal_overwrite(lib):
+    """k_t = e_t, g = 1, beta = 1: after d steps the state's rows are the v_t."""
+    rng = _rng(4)
+    d = 6
+    T = d
+    k = np.zeros((1, T, 1, d))
+    for t in range(T):
+        k[0, t, 0, t] = 1.0
+    q = rng.standard_normal((1, T, 1, d))
+    v = rng.standard_normal((1, T, 1, d))
+    h0 = rng.standard_normal((1, 1, d, d))
+    _, hT = oracle.gdn_sequential(q, k, v, np.zeros((1, T, 1)), np.ones((1, T, 1)), h0, lib=lib)
+    assert np.max(np.abs(hT[0, 0] - v[0, :, 0, :])) < 1e-14 * 8
+
+
+def pin_scalar_recurrence(lib):
+    """d = 1: s_t = g (1 - beta) s_{t-1} + beta sign(k) v_t; o_t = s_t sign(q)."""
+    rng = _rng(5)
+    T = 40
+    q, k, v, log_g, beta, h0 = _inputs(rng, 1, T, 1, 1, 1, 1, "qwen")
+    o, hT = oracle.gdn_sequential(q, k, v, log_g, beta, h0, q_scale=0.5, lib=lib)
+    s = h0[0, 0, 0, 0]
+    for t in range(T):
+        g = np.exp(log_g[0, t, 0])
+        bt = beta[0, t, 0]
+        s = g * (1.0 - bt) * s + bt * np.sign(k[0, t, 0, 0]) * v[0, t, 0, 0]
+        assert abs(o[0, t, 0, 0] - 0.5 * s * np.sign(q[0, t, 0, 0])) < 1e-14 * max(1, abs(s))
+    assert abs(hT[0, 0, 0, 0] - s) < 1e-14 * max(1, abs(s))
+
+
+def pin_exact_example(lib):
+    """A two-step, two-dimensional example worked in exact rational arithmetic.
+
+    k_1 = (3, 4) -> (3/5, 4/5); k_2 = (0, 2) -> (0, 1); q_t = (1, 0) raw;
+    g_1 = 1, g_2 = 1/2 (log g = -ln 2), beta = (1/2, 1); S0 = [[1, 2], [0, 1]].
+    """
+    F = Fraction
+    S = [[F(1), F(2)], [F(0), F(1)]]
+    ks = [(F(3, 5), F(4, 5)), (F(0), F(1))]
+    vs = [(F(1), F(-1)), (F(2), F(3))]
+    gs = [F(1), F(1, 2)]
+    bs = [F(1, 2), F(1)]
+    outs = []
+    for t in range(2):
+        kk, vv, g, b = ks[t], vs[t], gs[t], bs[t]
+        # S <- g (I - b k k^T) S + b k v^T, written entry by entry
+        M = [[(1 if i == j else 0) - b * kk[i] * kk[j] for j in range(2)] for i in range(2)]
+        S = [[g * sum(M[i][l] * S[l][j] for l in range(2)) + b * kk[i] * vv[j]
+              for j in range(2)] for i in range(2)]
+        outs.append([S[0][j] for j in range(2)])  # q = e_1 -> o = first row
+    q = np.array([[[[1.0, 0.0]], [[1.0, 0.0]]]])
+    k = np.array([[[[3.0, 4.0]], [[0.0, 2.0]]]])
+    v = np.array([[[[1.0, -1.0]], [[2.0, 3.0]]]])
+    log_g = np.array([[[0.0], [-np.log(2.0)]]])
+    beta = np.array([[[0.5], [1.0]]])
+    h0 = np.array([[[[1.0, 2.0], [0.0, 1.0]]]])
+    o, hT = oracle.gdn_sequential(q, k, v, log_g, beta, h0, lib=lib)
+    for t in range(2):
+        for j in range(2):
+            assert abs(o[0, t, 0, j] - float(outs[t][j])) < 1e-14
+    for i in range(2):
+        for j in range(2):
+            assert abs(hT[0, 0, i, j] - float(S[i][j])) < 1e-14
+
+
+def pin_split_invariance(lib):
+    """Carrying the final state across calls changes nothing (bitwise), incl. one token per call."""
+    rng = _rng(6)
+    B, T, Hk, Hv, d = 2, 23, 1, 3, 5
+    q, k, v, log_g, beta, h0 = _inputs(rng, B, T, Hk, Hv, d, d, "qwen")
+    o_ref, h_ref = oracle.gdn_sequential(q, k, v, log_g, beta, h0, lib=lib)
+    for cuts in ([0, 7, 23], [0, 1, 2, 16, 22, 23], list(range(T + 1))):
+        h = h0
+        parts = []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            o_p, h = oracle.gdn_sequential(q[:, a:b], k[:, a:b], v[:, a:b], log_g[:, a:b],
+                                           beta[:, a:b], h, lib=lib)
+            parts.append(o_p)
+        assert np.array_equal(np.concatenate(parts, axis=1), o_ref)
+        assert np.array_equal(h, h_ref)
+
+
+def pin_linearity(lib):
+    """o and S are jointly linear in (S0, V): f(S0, V) = f(S0, 0) + f(0, V)."""
+    rng = _rng(7)
+    B, T, Hk, Hv, d = 1, 15, 1, 2, 4
+    q, k, v, log_g, beta, h0 = _inputs(rng, B, T, Hk, Hv, d, d)
+    o, hT = oracle.gdn_sequential(q, k, v, log_g, beta, h0, lib=lib)
+    o1, h1 = oracle.gdn_sequential(q, k, np.zeros_like(v), log_g, beta, h0, lib=lib)
+    o2, h2 = oracle.gdn_sequential(q, k, v, log_g, beta, None, lib=lib)
+    assert _rel(o1 + o2, o) < 1e-12
+    assert _rel(h1 + h2, hT) < 1e-12
+    o3, h3 = oracle.gdn_sequential(q, k, 3.0 * v, log_g, beta, 3.0 * h0, lib=lib)
+    assert _rel(o3, 3.0 * o) < 1e-12 and _rel(h3, 3.0 * hT) < 1e-12
+
+
+def pin_nonexpansive(lib):
+    """beta in [0, 2], g <= 1: ||S_t||_2 <= g ||S_{t-1}||_2 + |beta| ||v_t||."""
+    rng = _rng(8)
+    T, d = 30, 6
+    q, k, v, log_g, _, h0 = _inputs(rng, 1, T, 1, 1, d, d, "qwen")
+    beta = rng.uniform(0.0, 2.0, size=(1, T, 1))
+    h = 5.0 * h0
+    for t in range(T):
+        _, h_new = oracle.gdn_sequential(q[:, t:t + 1], k[:, t:t + 1], v[:, t:t + 1],
+                                         log_g[:, t:t + 1], beta[:, t:t + 1], h, lib=lib)
+        lhs = np.linalg.norm(h_new[0, 0], 2)
+        rhs = np.exp(log_g[0, t, 0]) * np.linalg.norm(h[0, 0], 2) + \
+            abs(beta[0, t, 0]) * np.linalg.norm(v[0, t, 0])
+        assert lhs <= rhs * (1 + 1e-12)
+        h = h_new
+
+
+def pin_gqa_grouping(lib):
+    """Value head h reads key head h // (Hv/Hk); other key heads do not touch it."""
+    rng = _rng(9)
+    B, T, Hk, Hv, d = 1, 8, 2, 4, 5
+    q, k, v, log_g, beta, h0 = _inputs(rng, B, T, Hk, Hv, d, d)
+    o, hT = oracle.gdn_sequential(q, k, v, log_g, beta, h0, lib=lib)
+    q2, k2 = q.copy(), k.copy()
+    q2[:, :, 1] = rng.standard_normal(q2[:, :, 1].shape)
+    k2[:, :, 1] = rng.standard_normal(k2[:, :, 1].shape)
+    o2, h2 = oracle.gdn_sequential(q2, k2, v, log_g, beta, h0, lib=lib)
+    assert np.array_equal(o2[:, :, :2], o[:, :, :2]) and np.array_equal(h2[:, :2], hT[:, :2])
+    assert not np.allclose(o2[:, :, 2:], o[:, :, 2:])
+    # and value heads 0..1 equal a 1:1 run on key head 0 alone
+    o3, h3 = oracle.gdn_sequential(q[:, :, :1], k[:, :, :1], v[:, :, :2], log_g[:, :, :2],
+                                   beta[:, :, :2], h0[:, :2], lib=lib)
+    assert np.array_equal(o3, o[:, :, :2]) and np.array_equal(h3, hT[:, :2])
+
+
+def pin_normalisation(lib):
+    """q, k normalised: power-of-two rescaling is bitwise invisible; zero k writes nothing;
+    q_scale scales o only."""
+    rng = _rng(10)
+    B, T, Hk, Hv, d = 1, 10, 1, 2, 7
+    q, k, v, log_g, beta, h0 = _inputs(rng, B, T, Hk, Hv, d, d)
+    o, hT = oracle.gdn_sequential(q, k, v, log_g, beta, h0, lib=lib)
+    o2, h2 = oracle.gdn_sequential(8.0 * q, 0.25 * k, v, log_g, beta, h0, lib=lib)
+    assert np.array_equal(o, o2) and np.array_equal(hT, h2)
+    o3, h3 = oracle.gdn_sequential(q, k, v, log_g, beta, h0, q_scale=0.5, lib=lib)
+    assert np.array_equal(o3, 0.5 * o) and np.array_equal(h3, hT)
+    kz = np.zeros_like(k)
+    _, h4 = oracle.gdn_sequential(q, kz, v, log_g, beta, h0, lib=lib)
+    G = np.exp(np.sum(log_g[0], axis=0))
+    assert _rel(h4[0], G[:, None, None] * h0[0]) < 1e-13
+
+
+def pin_chunked_equals_sequential(lib):
+    """Chunked WY form with direct solve == token-serial form (tiny brute force)."""
+    rng = _rng(11)
+    cases = [(1, 1, 1, 1, 3), (4, 10, 2, 2, 3), (8, 15, 1, 3, 8), (16, 16, 2, 4, 1),
+             (32, 51, 1, 3, 8), (4, 37, 1, 1, 5), (64, 129, 1, 2, 8), (2, 7, 1, 1, 2)]
+    for C, T, Hk, Hv, d in cases:
+        for gate in ("uniform", "qwen"):
+            q, k, v, log_g, beta, h0 = _inputs(rng, 1, T, Hk, Hv, d, d, gate)
+            o_s, h_s = oracle.gdn_sequential(q, k, v, log_g, beta, h0, q_scale=0.75, lib=lib)
+            o_c, h_c = oracle.gdn_chunked(q, k, v, log_g, beta, h0, chunk=C, q_scale=0.75, lib=lib)
+            assert _rel(o_c, o_s) < 1e-12, (C, T, Hk, Hv, d, gate)
+            assert _rel(h_c, h_s) < 1e-12, (C, T, Hk, Hv, d, gate)
+
+
+def pin_triangular_inverse(lib):
+    """Forward substitution and Neumann doubling both invert I + A (A strictly lower)."""
+    rng = _rng(12)
+    for n in (1, 2, 3, 5, 8, 16, 33):
+        A = np.tril(rng.standard_normal((n, n)) * 0.3, -1)
+        junk = A + np.triu(rng.standard_normal((n, n)))  # upper part must be ignored
+        Ti = oracle.unit_lower_inverse(junk, lib=lib)
+        Tn = oracle.neumann_inverse(junk, lib=lib)
+        I = np.eye(n)
+        assert np.max(np.abs(Ti @ (I + A) - I)) < 1e-13
+        assert np.max(np.abs(Ti - np.linalg.inv(I + A))) < 1e-12
+        assert np.max(np.abs(Tn - Ti)) < 1e-12
+
+
+PINS = [
+    pin_identity_plumbing,
+    pin_matrix_form,
+    pin_unit_key_readback,
+    pin_no_write_closed_form,
+    pin_orthonormal_overwrite,
+    pin_scalar_recurrence,
+    pin_exact_example,
+    pin_split_invariance,
+    pin_linearity,
+    pin_nonexpansive,
+    pin_gqa_grouping,
+    pin_normalisation,
+    pin_chunked_equals_sequential,
+    pin_triangular_inverse,
+]
