@@ -1,0 +1,155 @@
+/*
+ * gdn.h -- C ABI of the gated delta rule (Gated DeltaNet layer core) for
+ * AMD Instinct MI355X (gfx950).  Library: libgdn.so.
+ *
+ * The operation (per batch b and value head h, key head hk = h / (Hv/Hk)):
+ *
+ *     S_t = g_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = q_scale * S_t^T q_t,            g_t = exp(log_g_t)
+ *
+ * with q_t, k_t optionally L2-normalised in the kernels (x / max(|x|, 1e-6)).
+ * This is the five-step per-token update of "Qwen3.5 Gated Delta Net NKI
+ * Kernel for AWS Neuron" (Hugging Face model card), section "How It Works":
+ * decay the state, read S^T k, delta = beta (v - read), write k delta^T, and
+ * read the output from the updated state.  The same card's "Correctness
+ * Contract" fixes log g <= 0 for Qwen gates (nothing is clamped here either)
+ * and makes every (batch, head) independent.  Key heads are shared by
+ * consecutive groups of Hv/Hk value heads, as in the 16-key / 48-value-head
+ * layout of "Add Qwen3.6-27B contrib model with vLLM APC baseline", table
+ * "Architecture".
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library allocates no device memory and keeps no mutable global state.
+ *  - Tensors are dense, row-major, innermost dimension last, exactly as listed;
+ *    no strides.  Every pointer must be 16-byte aligned.
+ *  - q, k, v and o share one storage dtype (gdn_problem.dtype).  log_g, beta
+ *    and the recurrent states are always fp32.
+ *  - hip_stream is a hipStream_t passed as void*; NULL means the null stream.
+ *    Work is enqueued asynchronously; the library never synchronises.
+ *  - All argument checks run on the host before anything is enqueued: on any
+ *    error the call returns a non-zero gdn_status and enqueues nothing.  A
+ *    launch failure reported by the HIP runtime returns GDN_ERR_HIP.  Faults
+ *    during execution surface at the caller's next synchronisation, as for
+ *    any HIP work.
+ *  - Results are bitwise deterministic for identical inputs and launch
+ *    parameters (no atomics, fixed reduction orders).
+ *  - Calls on different streams are independent and thread-safe provided
+ *    their output buffers do not overlap.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_DTYPE_F32 = 0,   /* IEEE binary32 */
+    GDN_DTYPE_BF16 = 1   /* bfloat16; kernels accumulate in fp32 and round to
+                            nearest-even when storing o */
+} gdn_dtype;
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+    GDN_ERR_BAD_SHAPE = 2,    /* negative size, Hv % Hk != 0, decode T != 1, ... */
+    GDN_ERR_UNSUPPORTED = 3,  /* head dim / chunk / dtype outside the built kernels */
+    GDN_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned */
+    GDN_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required */
+    GDN_ERR_HIP = 6,          /* the HIP runtime refused the launch */
+    GDN_ERR_ALIAS = 7         /* an output overlaps an input it may not alias */
+} gdn_status;
+
+/* Per-call sizes and options. */
+typedef struct {
+    int32_t B;         /* sequences in the batch, >= 0 */
+    int32_t T;         /* tokens per sequence in this call, >= 0 (decode: 1) */
+    int32_t Hk;        /* key heads (shared by q and k), >= 1 */
+    int32_t Hv;        /* value heads, a multiple of Hk */
+    int32_t dk;        /* key head dim: 64 or 128 */
+    int32_t dv;        /* value head dim: must equal dk */
+    int32_t chunk;     /* prefill chunk length C: 16, 32 or 64 (0 selects 64);
+                          ignored by decode */
+    int32_t dtype;     /* gdn_dtype of q, k, v, o */
+    int32_t qk_l2norm; /* 1: L2-normalise q and k per token inside the kernels;
+                          0: use them as given */
+    float q_scale;     /* multiplies every output (1.0 for the plain rule) */
+} gdn_problem;
+
+/*
+ * Workspace bytes that gdn_chunk_prefill needs for this problem (0 is
+ * possible).  Returns 0 also for an invalid problem; gdn_chunk_prefill reports
+ * the error.  The caller allocates the workspace; its contents need no
+ * initialisation and are meaningless after the call.
+ */
+size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* problem);
+
+/*
+ * Chunked prefill (context encoding) of T tokens for B sequences.
+ *
+ * Defined by the recurrence above, evaluated chunk-parallel: inside each chunk
+ * of C tokens the decay-masked beta K K^T system is solved directly (forward
+ * substitution, never a Neumann power series), as in "Qwen3.6: Fused
+ * DeltaNet Direct-Solve Follow-Up", sections "Why This Exists" and
+ * "Implementation Details"; the state is handed from chunk to chunk in order.
+ * A last chunk shorter than C is allowed.  The result equals the token-serial
+ * recurrence up to rounding; splitting a sequence at multiples of C across
+ * calls (carrying hT into the next h0) gives bitwise the same o and hT.
+ *
+ *   q, k   [B, T, Hk, dk]   dtype
+ *   v      [B, T, Hv, dv]   dtype
+ *   log_g  [B, T, Hv]       fp32, natural-log decay (<= 0 for Qwen gates)
+ *   beta   [B, T, Hv]       fp32
+ *   h0     [B, Hv, dk, dv]  fp32 initial state, or NULL for zeros
+ *   hT     [B, Hv, dk, dv]  fp32 final state, or NULL to drop it; may be the
+ *                           same pointer as h0 (in-place carry), may not
+ *                           otherwise overlap it
+ *   o      [B, T, Hv, dv]   dtype, written
+ *   workspace / workspace_bytes: see gdn_chunk_prefill_workspace_bytes
+ *
+ * T == 0 writes hT = h0 (or zeros) and nothing else.
+ */
+gdn_status gdn_chunk_prefill(const gdn_problem* problem,
+                             const void* q, const void* k, const void* v,
+                             const float* log_g, const float* beta,
+                             const float* h0, float* hT, void* o,
+                             void* workspace, size_t workspace_bytes,
+                             void* hip_stream);
+
+/*
+ * One decode step (one token per sequence) updating the state in place.
+ *
+ * Evaluates the five steps for a single token with one read and one write of
+ * each state: a = S^T k and c = S^T q come from the same pass over the old
+ * state, then delta = beta (v - g a), o = q_scale (g c + delta (k . q)), and
+ * S <- g S + k delta^T is stored to the same addresses.
+ * problem->T must be 1; problem->chunk is ignored.
+ *
+ *   q, k   [B, Hk, dk]      dtype
+ *   v      [B, Hv, dv]      dtype
+ *   log_g  [B, Hv]          fp32
+ *   beta   [B, Hv]          fp32
+ *   state  [B, Hv, dk, dv]  fp32, read and overwritten in place
+ *   o      [B, Hv, dv]      dtype, written
+ */
+gdn_status gdn_decode_step(const gdn_problem* problem,
+                           const void* q, const void* k, const void* v,
+                           const float* log_g, const float* beta,
+                           float* state, void* o, void* hip_stream);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* gdn_status_string(gdn_status status);
+
+/* GDN_ABI_VERSION of the built library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

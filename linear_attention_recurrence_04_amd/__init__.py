@@ -1,5 +1,10 @@
 """Gated DeltaNet (gated delta rule) layer core for MI355X (gfx950).
 
-The HIP library (``libgdn.so``) is loaded on first use by the binding, so the
-seeded input generator can be imported on machines without a GPU.
+``gdn_chunk_prefill`` and ``gdn_decode_step`` call the C ABI of libgdn.so
+(include/gdn.h).  The library is loaded on first use, so the seeded input
+generator (``.inputs``) imports on machines without a GPU; a call without the
+built library raises.
 """
+from .binding import (GDN_DTYPE_BF16, GDN_DTYPE_F32, GdnError, GdnProblem,  # noqa: F401
+                      gdn_abi_version, gdn_chunk_prefill, gdn_chunk_prefill_workspace_bytes,
+                      gdn_decode_step, gdn_status_string, make_problem)

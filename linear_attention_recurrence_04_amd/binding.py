@@ -1,0 +1,195 @@
+"""Thin ctypes binding of libgdn.so (include/gdn.h).
+
+Argument marshalling only: checks that torch tensors have the layout the C ABI
+expects, allocates outputs with torch's caching allocator, and passes raw
+device pointers plus torch's current HIP stream.  Every step of the
+computation runs in the HIP kernels; there is no CPU or PyTorch fallback --
+a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libgdn.so")
+
+GDN_DTYPE_F32 = 0
+GDN_DTYPE_BF16 = 1
+GDN_OK = 0
+STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
+                3: "GDN_ERR_UNSUPPORTED", 4: "GDN_ERR_MISALIGNED", 5: "GDN_ERR_WORKSPACE",
+                6: "GDN_ERR_HIP", 7: "GDN_ERR_ALIAS"}
+
+
+class GdnProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hk", ctypes.c_int32),
+                ("Hv", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("qk_l2norm", ctypes.c_int32), ("q_scale", ctypes.c_float)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libgdn.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError(f"{LIBRARY} is missing: build it with "
+                           "`python -m linear_attention_recurrence_04_amd.build`")
+    L = ctypes.CDLL(LIBRARY)
+    vp, fp, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
+    pp = ctypes.POINTER(GdnProblem)
+    L.gdn_abi_version.restype = ctypes.c_int
+    L.gdn_abi_version.argtypes = []
+    L.gdn_status_string.restype = ctypes.c_char_p
+    L.gdn_status_string.argtypes = [ctypes.c_int]
+    L.gdn_chunk_prefill_workspace_bytes.restype = sz
+    L.gdn_chunk_prefill_workspace_bytes.argtypes = [pp]
+    L.gdn_chunk_prefill.restype = ctypes.c_int
+    L.gdn_chunk_prefill.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, vp, vp, sz, vp]
+    L.gdn_decode_step.restype = ctypes.c_int
+    L.gdn_decode_step.argtypes = [pp, vp, vp, vp, fp, fp, fp, vp, vp]
+    _lib = L
+    return L
+
+
+def gdn_abi_version() -> int:
+    return lib().gdn_abi_version()
+
+
+def gdn_status_string(status: int) -> str:
+    return lib().gdn_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, gdn_status_string(status))
+
+
+def make_problem(B, T, Hk, Hv, dk, dv, *, chunk=64, dtype=GDN_DTYPE_BF16, qk_l2norm=True,
+                 q_scale=1.0) -> GdnProblem:
+    return GdnProblem(int(B), int(T), int(Hk), int(Hv), int(dk), int(dv), int(chunk),
+                      int(dtype), int(bool(qk_l2norm)), float(q_scale))
+
+
+def gdn_chunk_prefill_workspace_bytes(problem: GdnProblem) -> int:
+    return int(lib().gdn_chunk_prefill_workspace_bytes(ctypes.byref(problem)))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing calls
+# ---------------------------------------------------------------------------
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return GDN_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return GDN_DTYPE_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def gdn_chunk_prefill(q, k, v, log_g, beta, h0=None, *, chunk: int = 64,
+                      qk_l2norm: bool = True, q_scale: float = 1.0, out=None, hT=None,
+                      want_state: bool = True, workspace=None,
+                      stream=None) -> Tuple[object, object]:
+    """Chunked prefill.  q, k [B,T,Hk,d]; v [B,T,Hv,d]; log_g, beta [B,T,Hv] fp32;
+    h0 [B,Hv,d,d] fp32 or None.  Returns (o [B,T,Hv,d], hT or None).
+    ``hT`` may be passed (even ``hT is h0``) to receive the state in place."""
+    torch = _torch()
+    _need(q, "q")
+    dt = _dtype_code(q)
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    _need(k, "k", q.dtype, q.shape)
+    _need(v, "v", q.dtype, (B, T, Hv, dv))
+    _need(log_g, "log_g", torch.float32, (B, T, Hv))
+    _need(beta, "beta", torch.float32, (B, T, Hv))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, Hv, dk, dv))
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(out, "out", q.dtype, (B, T, Hv, dv))
+    if hT is None and want_state:
+        hT = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=q.device)
+    elif hT is not None:
+        _need(hT, "hT", torch.float32, (B, Hv, dk, dv))
+    prob = make_problem(B, T, Hk, Hv, dk, dv, chunk=chunk, dtype=dt, qk_l2norm=qk_l2norm,
+                        q_scale=q_scale)
+    need = gdn_chunk_prefill_workspace_bytes(prob)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().gdn_chunk_prefill(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g),
+                                 _ptr(beta), _ptr(h0), _ptr(hT), _ptr(out), _ptr(workspace),
+                                 ws_bytes, _stream(stream))
+    _check(st)
+    return out, hT
+
+
+def gdn_decode_step(q, k, v, log_g, beta, state, *, qk_l2norm: bool = True,
+                    q_scale: float = 1.0, out=None, stream=None):
+    """One decode step.  q, k [B,Hk,d]; v [B,Hv,d]; log_g, beta [B,Hv] fp32;
+    state [B,Hv,d,d] fp32 is updated in place.  Returns o [B,Hv,d]."""
+    torch = _torch()
+    _need(q, "q")
+    dt = _dtype_code(q)
+    B, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    _need(k, "k", q.dtype, q.shape)
+    _need(v, "v", q.dtype, (B, Hv, dv))
+    _need(log_g, "log_g", torch.float32, (B, Hv))
+    _need(beta, "beta", torch.float32, (B, Hv))
+    _need(state, "state", torch.float32, (B, Hv, dk, dv))
+    if out is None:
+        out = torch.empty((B, Hv, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(out, "out", q.dtype, (B, Hv, dv))
+    prob = make_problem(B, 1, Hk, Hv, dk, dv, chunk=0, dtype=dt, qk_l2norm=qk_l2norm,
+                        q_scale=q_scale)
+    st = lib().gdn_decode_step(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g),
+                               _ptr(beta), _ptr(state), _ptr(out), _stream(stream))
+    _check(st)
+    return out

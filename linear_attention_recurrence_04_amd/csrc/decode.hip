@@ -1,0 +1,160 @@
+// decode.hip -- single-token gated-delta-rule step with the state updated in place.
+//
+// Per (batch b, value head h) the five steps of "Qwen3.5 Gated Delta Net NKI
+// Kernel for AWS Neuron", section "How It Works", are fused into ONE pass over
+// the fp32 state:
+//     a = S^T k_hat,  c = S^T q_hat          (both from the old state)
+//     delta = beta (v - g a)                  (the read of the decayed state)
+//     o = q_scale (g c + delta (k_hat . q_hat))   (= (g S + k delta^T)^T q_hat)
+//     S <- g S + k_hat delta^T                (stored to the same addresses)
+// so each step reads and writes every state element exactly once.  That is
+// the whole cost: the state is 4*dk*dv bytes per head against ~7*dk*dv flops,
+// so the kernel is bound by HBM bandwidth.
+//
+// Mapping: one workgroup of 256 threads per (b, h).  A thread owns a float4
+// column strip of D/RG rows (RG = row groups), held in VGPRs between the read
+// and the write; rows are interleaved so each wave load covers whole 512-byte
+// rows (fully coalesced 16-byte accesses).  Column reductions over the rows
+// combine per-thread partials in LDS in a fixed order (deterministic).
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const float* __restrict__ log_g, const float* __restrict__ beta,
+    float* __restrict__ state, TIn* __restrict__ o,
+    int Hk, int Hv, int l2norm, float q_scale) {
+    constexpr int NT = 256;
+    constexpr int CG = D / 4;     // float4 column groups per row
+    constexpr int RG = NT / CG;   // row groups
+    constexpr int RPT = D / RG;   // rows per thread
+    static_assert(RPT * RG == D && CG * RG == NT, "decode tiling");
+
+    const int bh = blockIdx.x;    // b * Hv + h
+    const int b = bh / Hv;
+    const int h = bh - b * Hv;
+    const int hk = h / (Hv / Hk);
+    const int tid = threadIdx.x;
+    const int cg = tid % CG;
+    const int rg = tid / CG;
+
+    __shared__ float kh[D];
+    __shared__ float qh[D];
+    __shared__ float red[2][RG][D];
+    __shared__ float wsum[NT / 64][3];
+    __shared__ float dl[D];
+
+    float* S = state + (size_t)bh * D * D;
+
+    // 1. stream this head's state into registers (all loads in flight at once)
+    float4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        s[i] = *reinterpret_cast<const float4*>(S + (size_t)(rg + RG * i) * D + 4 * cg);
+
+    // 2. q, k of the key head, normalised in fp32
+    float kv = 0.f, qv = 0.f;
+    if (tid < D) {
+        const size_t off = ((size_t)b * Hk + hk) * D + tid;
+        kv = to_f32(k[off]);
+        qv = to_f32(q[off]);
+    }
+    float ssk = group_sum<64>(kv * kv);
+    float ssq = group_sum<64>(qv * qv);
+    if ((tid & 63) == 0) {
+        wsum[tid >> 6][0] = ssk;
+        wsum[tid >> 6][1] = ssq;
+    }
+    __syncthreads();
+    float rk = 1.f, rq = 1.f;
+    if (l2norm) {
+        float tk = 0.f, tq = 0.f;
+#pragma unroll
+        for (int w = 0; w < (D + 63) / 64; ++w) {
+            tk += wsum[w][0];
+            tq += wsum[w][1];
+        }
+        rk = inv_l2(tk);
+        rq = inv_l2(tq);
+    }
+    if (tid < D) {
+        kh[tid] = kv * rk;
+        qh[tid] = qv * rq;
+    }
+    __syncthreads();
+    // k_hat . q_hat (needed by the fused output identity)
+    float kq_part = (tid < D) ? kh[tid] * qh[tid] : 0.f;
+    kq_part = group_sum<64>(kq_part);
+    if ((tid & 63) == 0) wsum[tid >> 6][2] = kq_part;
+
+    // 3. per-thread partial reads a = S^T k, c = S^T q over its rows
+    float pa[4] = {0.f, 0.f, 0.f, 0.f}, pc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const float kr = kh[rg + RG * i];
+        const float qr = qh[rg + RG * i];
+        pa[0] += s[i].x * kr; pa[1] += s[i].y * kr; pa[2] += s[i].z * kr; pa[3] += s[i].w * kr;
+        pc[0] += s[i].x * qr; pc[1] += s[i].y * qr; pc[2] += s[i].z * qr; pc[3] += s[i].w * qr;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        red[0][rg][4 * cg + c] = pa[c];
+        red[1][rg][4 * cg + c] = pc[c];
+    }
+    __syncthreads();
+
+    // 4. column totals, delta and the output (one thread per column)
+    const float g = expf(log_g[bh]);
+    const float bt = beta[bh];
+    if (tid < D) {
+        float a = 0.f, c = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            a += red[0][r][tid];
+            c += red[1][r][tid];
+        }
+        float kq = 0.f;
+#pragma unroll
+        for (int w = 0; w < (D + 63) / 64; ++w) kq += wsum[w][2];
+        const float vj = to_f32(v[(size_t)bh * D + tid]);
+        const float delta = bt * (vj - g * a);
+        dl[tid] = delta;
+        o[(size_t)bh * D + tid] = from_f32<TIn>(q_scale * (g * c + delta * kq));
+    }
+    __syncthreads();
+
+    // 5. S <- g S + k delta^T, written back over the same addresses
+    const float4 d4 = *reinterpret_cast<const float4*>(&dl[4 * cg]);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const float kr = kh[rg + RG * i];
+        float4 n;
+        n.x = g * s[i].x + kr * d4.x;
+        n.y = g * s[i].y + kr * d4.y;
+        n.z = g * s[i].z + kr * d4.z;
+        n.w = g * s[i].w + kr * d4.w;
+        *reinterpret_cast<float4*>(S + (size_t)(rg + RG * i) * D + 4 * cg) = n;
+    }
+}
+
+template <int D, typename TIn>
+static hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+    const int blocks = a.B * a.Hv;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_step_kernel<D, TIn>), dim3(blocks), dim3(256), 0, stream,
+                       static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                       static_cast<const TIn*>(a.v), a.log_g, a.beta, a.state,
+                       static_cast<TIn*>(a.o), a.Hk, a.Hv, a.l2norm, a.q_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream) {
+    if (a.D == 128)
+        return a.bf16 ? launch_decode<128, bf16_t>(a, stream) : launch_decode<128, float>(a, stream);
+    return a.bf16 ? launch_decode<64, bf16_t>(a, stream) : launch_decode<64, float>(a, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,166 @@
+// gdn_api.cpp -- the C ABI (include/gdn.h): argument checks and kernel dispatch.
+//
+// Every check runs on the host before anything is enqueued, so a rejected call
+// leaves the stream untouched.  The checks turn the forward-time assertions of
+// "Qwen3.5 Gated Delta Net NKI Kernel for AWS Neuron" ("Correctness Contract":
+// head dims equal and supported) into status codes.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+
+bool overlaps(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared checks of the problem description.  `decode` selects the decode rules.
+gdn_status check_problem(const gdn_problem* p, bool decode) {
+    if (!p) return GDN_ERR_NULL_POINTER;
+    if (p->B < 0 || p->T < 0 || p->Hk < 1 || p->Hv < 1) return GDN_ERR_BAD_SHAPE;
+    if (p->Hv % p->Hk != 0) return GDN_ERR_BAD_SHAPE;
+    if (decode && p->T != 1) return GDN_ERR_BAD_SHAPE;
+    if (p->dk != p->dv) return GDN_ERR_UNSUPPORTED;
+    if (p->dk != 64 && p->dk != 128) return GDN_ERR_UNSUPPORTED;
+    if (p->dtype != GDN_DTYPE_F32 && p->dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+    if (p->qk_l2norm != 0 && p->qk_l2norm != 1) return GDN_ERR_UNSUPPORTED;
+    if (!decode && p->chunk != 0 && p->chunk != 16 && p->chunk != 32 && p->chunk != 64)
+        return GDN_ERR_UNSUPPORTED;
+    // grid limits: one workgroup row per (b, h); sizes must fit the index math
+    const long long bh = (long long)p->B * p->Hv;
+    if (bh > 0x7fffffffLL) return GDN_ERR_BAD_SHAPE;
+    const long long elems = (long long)p->B * p->T * p->Hv * p->dv;
+    if (elems > (1LL << 46)) return GDN_ERR_BAD_SHAPE;
+    return GDN_OK;
+}
+
+size_t dsize(const gdn_problem* p) { return p->dtype == GDN_DTYPE_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case GDN_ERR_BAD_SHAPE: return "invalid sizes (negative, Hv not a multiple of Hk, decode T != 1, or too large)";
+        case GDN_ERR_UNSUPPORTED: return "unsupported head dim, chunk, dtype or flag (dk == dv in {64,128}; chunk in {0,16,32,64})";
+        case GDN_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
+        case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+        case GDN_ERR_ALIAS: return "an output buffer overlaps an input";
+    }
+    return "unknown gdn_status";
+}
+
+size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* p) {
+    if (check_problem(p, false) != GDN_OK) return 0;
+    return 0;  // the built prefill kernels keep every intermediate on chip
+}
+
+gdn_status gdn_chunk_prefill(const gdn_problem* p, const void* q, const void* k, const void* v,
+                             const float* log_g, const float* beta, const float* h0, float* hT,
+                             void* o, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    gdn_status st = check_problem(p, false);
+    if (st != GDN_OK) return st;
+    const size_t es = dsize(p);
+    const size_t BT = (size_t)p->B * p->T;
+    const size_t qk_bytes = BT * p->Hk * p->dk * es;
+    const size_t v_bytes = BT * p->Hv * p->dv * es;
+    const size_t g_bytes = BT * p->Hv * sizeof(float);
+    const size_t s_bytes = (size_t)p->B * p->Hv * p->dk * p->dv * sizeof(float);
+
+    if (BT > 0 && (!q || !k || !v || !log_g || !beta || !o)) return GDN_ERR_NULL_POINTER;
+    const void* ptrs[] = {q, k, v, log_g, beta, h0, hT, o, workspace};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
+
+    const size_t need_ws = gdn_chunk_prefill_workspace_bytes(p);
+    if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return GDN_ERR_WORKSPACE;
+
+    // outputs against inputs: hT may be exactly h0, nothing else may overlap
+    const Range ins[] = {range_of(q, BT ? qk_bytes : 0), range_of(k, BT ? qk_bytes : 0),
+                         range_of(v, BT ? v_bytes : 0), range_of(log_g, BT ? g_bytes : 0),
+                         range_of(beta, BT ? g_bytes : 0)};
+    const Range r_o = range_of(o, BT ? v_bytes : 0);
+    const Range r_hT = range_of(hT, hT ? s_bytes : 0);
+    const Range r_h0 = range_of(h0, h0 ? s_bytes : 0);
+    const Range r_ws = range_of(workspace, workspace ? need_ws : 0);
+    for (const Range& in : ins) {
+        if (overlaps(in, r_o) || overlaps(in, r_hT) || overlaps(in, r_ws)) return GDN_ERR_ALIAS;
+    }
+    if (overlaps(r_o, r_hT) || overlaps(r_o, r_h0) || overlaps(r_o, r_ws)) return GDN_ERR_ALIAS;
+    if (overlaps(r_hT, r_ws) || overlaps(r_h0, r_ws)) return GDN_ERR_ALIAS;
+    if (hT && h0 && hT != h0 && overlaps(r_hT, r_h0)) return GDN_ERR_ALIAS;
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (p->B == 0 || p->Hv == 0) return GDN_OK;
+    hipError_t err;
+    if (p->T == 0) {
+        err = gdn::launch_state_copy(h0, hT, s_bytes / sizeof(float), stream);
+        return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    }
+    gdn::PrefillArgs a;
+    a.B = p->B; a.T = p->T; a.Hk = p->Hk; a.Hv = p->Hv; a.D = p->dk;
+    a.C = p->chunk ? p->chunk : 64;
+    a.bf16 = p->dtype == GDN_DTYPE_BF16;
+    a.l2norm = p->qk_l2norm;
+    a.q_scale = p->q_scale;
+    a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
+    a.h0 = h0; a.hT = hT; a.o = o; a.ws = workspace; a.ws_bytes = workspace_bytes;
+    err = gdn::launch_prefill_generic(a, stream);
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, const void* v,
+                           const float* log_g, const float* beta, float* state, void* o,
+                           void* hip_stream) {
+    gdn_status st = check_problem(p, true);
+    if (st != GDN_OK) return st;
+    if (p->B > 0 && (!q || !k || !v || !log_g || !beta || !state || !o))
+        return GDN_ERR_NULL_POINTER;
+    const void* ptrs[] = {q, k, v, log_g, beta, state, o};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
+    const size_t es = dsize(p);
+    const size_t B = (size_t)p->B;
+    const Range r_state = range_of(state, B * p->Hv * p->dk * p->dv * sizeof(float));
+    const Range r_o = range_of(o, B * p->Hv * p->dv * es);
+    const Range ins[] = {range_of(q, B * p->Hk * p->dk * es), range_of(k, B * p->Hk * p->dk * es),
+                         range_of(v, B * p->Hv * p->dv * es), range_of(log_g, B * p->Hv * 4),
+                         range_of(beta, B * p->Hv * 4)};
+    for (const Range& in : ins)
+        if (overlaps(in, r_state) || overlaps(in, r_o)) return GDN_ERR_ALIAS;
+    if (overlaps(r_state, r_o)) return GDN_ERR_ALIAS;
+    if (p->B == 0) return GDN_OK;
+
+    gdn::DecodeArgs a;
+    a.B = p->B; a.Hk = p->Hk; a.Hv = p->Hv; a.D = p->dk;
+    a.bf16 = p->dtype == GDN_DTYPE_BF16;
+    a.l2norm = p->qk_l2norm;
+    a.q_scale = p->q_scale;
+    a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta; a.state = state; a.o = o;
+    const hipError_t err = gdn::launch_decode_step(a, static_cast<hipStream_t>(hip_stream));
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// gdn_device.h -- small device helpers shared by the gated-delta-rule kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// bfloat16 is handled as its raw 16-bit pattern.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Round-to-nearest-even conversion, NaN kept quiet.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>(0x7fc0);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
+
+// Butterfly sum over `width` consecutive lanes (width a power of two <= 64);
+// every lane of the group receives the total, in the same order on all lanes.
+template <int width>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int m = width / 2; m >= 1; m /= 2) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+// 1 / max(sqrt(ss), 1e-6): the L2-normalisation factor used by every kernel.
+__device__ __forceinline__ float inv_l2(float ss) {
+    return 1.0f / fmaxf(sqrtf(ss), 1e-6f);
+}
+
+}  // namespace gdn

@@ -1,0 +1,43 @@
+// gdn_launch.h -- internal launch interface between the C ABI and the kernels.
+// Arguments here are already validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace gdn {
+
+struct DecodeArgs {
+    int B, Hk, Hv, D;
+    bool bf16;
+    int l2norm;
+    float q_scale;
+    const void *q, *k, *v;
+    const float *log_g, *beta;
+    float* state;
+    void* o;
+};
+
+struct PrefillArgs {
+    int B, T, Hk, Hv, D, C;
+    bool bf16;
+    int l2norm;
+    float q_scale;
+    const void *q, *k, *v;
+    const float *log_g, *beta;
+    const float* h0;   // may be null (zeros)
+    float* hT;         // may be null; may equal h0
+    void* o;
+    void* ws;          // workspace (validated size)
+    size_t ws_bytes;
+};
+
+hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
+
+// Portable path: any supported (D, C, dtype); fp32 arithmetic throughout.
+hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t stream);
+
+// hT = h0 (or zeros) without touching anything else (T == 0).
+hipError_t launch_state_copy(const float* h0, float* hT, size_t n, hipStream_t stream);
+
+}  // namespace gdn

@@ -162,6 +162,26 @@ def make_prefill(p: Problem, seed: int, T: Optional[int] = None) -> dict:
     return {"q": q, "k": k, "v": v, "log_g": log_g, "beta": beta, "h0": h0}
 
 
+def make_long_segment(p: Problem, seed: int, call: int) -> dict:
+    """Inputs of one call of a long prompt processed in fixed-size calls.
+
+    Call ``call`` covers tokens [call*Tc, (call+1)*Tc), Tc = p.extra["call_tokens"],
+    drawn from its own stream so any call is reproducible alone; A_log (a
+    per-value-head model parameter) is shared by every call.  Same recipe and
+    draw order as make_prefill; the initial state of the prompt is zero.
+    """
+    Tc = p.extra["call_tokens"]
+    B, Hk, Hv, dk, dv = p.B, p.Hk, p.Hv, p.dk, p.dv
+    a_log = np.random.default_rng([seed, 7]).uniform(-2.0, 1.0, size=(Hv,))
+    rng = np.random.default_rng([seed, 1000 + call])
+    q = _store(rng.standard_normal((B, Tc, Hk, dk)), p.dtype)
+    k = _store(rng.standard_normal((B, Tc, Hk, dk)), p.dtype)
+    v = _store(rng.standard_normal((B, Tc, Hv, dv)), p.dtype)
+    beta = sigmoid(rng.standard_normal((B, Tc, Hv))).astype(np.float32)
+    log_g = _gates(rng, (B, Tc), Hv, p.gate, p.gate_lo, p.gate_hi, a_log=a_log)
+    return {"q": q, "k": k, "v": v, "log_g": log_g, "beta": beta, "h0": None}
+
+
 def make_decode_state(p: DecodeProblem, seed: int) -> np.ndarray:
     """Initial decode state [B,Hv,dk,dv] ~ N(0, 0.02), float32."""
     rng = np.random.default_rng([seed, 1])
