@@ -1,0 +1,293 @@
+"""Benchmark of the gated-delta-rule hot path on one MI355X.
+
+One "step" is one chunked-prefill call of the 27B-shaped workload
+(B=1, T=16384, 16 key heads shared 1:3 by 48 value heads, d=128, bf16 q/k/v,
+fp32 gates and state, chunk 64).  ``value`` is prefill tokens/s.  The decode
+half of the metric (B=64 sequences, same heads, one token per step for 1000
+steps, fp32 state updated in place) is timed in the same run and reported
+under "decode" as state-update HBM GB/s and tokens/s.
+
+Inputs are seeded synthetic tensors already resident in HBM when the timed
+region starts.  Kernel time comes from HIP events recorded on the stream the
+kernels are launched on.  The fp64 oracle (test infrastructure) is timed on
+host cores on a bounded sample of the same prefill workload as "cpu_baseline".
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from linear_attention_recurrence_04_amd import inputs as gi  # noqa: E402
+
+METRIC = "GDN prefill tokens/s (Hk16/Hv48, d=128) + decode state-update HBM GB/s"
+
+# MI355X published peaks
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "linear_attention_recurrence_04_amd", "csrc")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (per call), stated once here and in the design notes
+# ---------------------------------------------------------------------------
+
+
+def prefill_useful_flops(p) -> float:
+    """Useful flops of the chunked method per call: per token and value head
+    6 dk dv (three state products) + C (dk + 2 dv) (triangular halves of the
+    intra-chunk products) + 2 C dk / r (the two Gram products, once per key head)."""
+    r = p.Hv // p.Hk
+    per = 6 * p.dk * p.dv + p.chunk * (p.dk + 2 * p.dv) + 2 * p.chunk * p.dk / r
+    return per * p.B * p.T * p.Hv
+
+
+def prefill_bytes(p, h0: bool = True) -> float:
+    """Minimum HBM bytes of one call: read q, k, v, log_g, beta, h0; write o, hT."""
+    s = 2 if p.dtype == "bf16" else 4
+    per_token = 2 * p.Hk * p.dk * s + p.Hv * p.dv * s + p.Hv * p.dv * s + 8 * p.Hv
+    state = p.B * p.Hv * p.dk * p.dv * 4
+    return p.B * p.T * per_token + state * (1 + (1 if h0 else 0))
+
+
+def decode_bytes(d) -> float:
+    """Minimum HBM bytes of one decode step: the state read and written once,
+    plus q, k, v, o (bf16) and log_g, beta (fp32)."""
+    s = 2 if d.dtype == "bf16" else 4
+    return 2 * d.B * d.Hv * d.dk * d.dv * 4 + d.B * (2 * d.Hk * d.dk * s + 2 * d.Hv * d.dv * s + 8 * d.Hv)
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(kernel_key: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
+    or None when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tab = json.load(f)
+    ent = tab.get(kernel_key)
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return float(ent["bytes_per_launch"])
+
+
+# ---------------------------------------------------------------------------
+
+
+def time_stream(torch, fn, steps: int):
+    """Run fn() `steps` times between two events on the current stream."""
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop)  # ms
+
+
+def bench_prefill(torch, gdn, p, steps, warmup):
+    log(f"prefill workload {p.name}: generating inputs")
+    inp = gi.make_prefill(p, 0)
+    dev = {n: torch.from_numpy(inp[n]).cuda() for n in ("q", "k", "v", "log_g", "beta", "h0")}
+    for n in ("q", "k", "v"):
+        dev[n] = dev[n].to(torch.bfloat16) if p.dtype == "bf16" else dev[n]
+    out = torch.empty((p.B, p.T, p.Hv, p.dv), dtype=dev["q"].dtype, device="cuda")
+    hT = torch.empty((p.B, p.Hv, p.dk, p.dv), dtype=torch.float32, device="cuda")
+    prob = gdn.make_problem(p.B, p.T, p.Hk, p.Hv, p.dk, p.dv, chunk=p.chunk,
+                            dtype=gdn.GDN_DTYPE_BF16 if p.dtype == "bf16" else gdn.GDN_DTYPE_F32)
+    ws_bytes = gdn.gdn_chunk_prefill_workspace_bytes(prob)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        gdn.gdn_chunk_prefill(dev["q"], dev["k"], dev["v"], dev["log_g"], dev["beta"], dev["h0"],
+                              chunk=p.chunk, out=out, hT=hT, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    log(f"prefill: timing {steps} steps")
+    ms = time_stream(torch, call, steps)
+    return ms / steps, prob
+
+
+def bench_decode(torch, gdn, d, steps, warmup):
+    log(f"decode workload {d.name}: generating {steps} steps of inputs")
+    st = gi.make_decode_steps(d, 0, steps=steps)
+    dv = {n: torch.from_numpy(st[n]).cuda() for n in st}
+    for n in ("q", "k", "v"):
+        dv[n] = dv[n].to(torch.bfloat16)
+    state0 = torch.from_numpy(gi.make_decode_state(d, 0)).cuda()
+    state = state0.clone()
+    out = torch.empty((d.B, d.Hv, d.dv), dtype=torch.bfloat16, device="cuda")
+    idx = [0]
+
+    def call():
+        s = idx[0]
+        gdn.gdn_decode_step(dv["q"][s], dv["k"][s], dv["v"][s], dv["log_g"][s], dv["beta"][s],
+                            state, out=out)
+        idx[0] = (s + 1) % steps
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    state.copy_(state0)
+    idx[0] = 0
+    log(f"decode: timing {steps} steps")
+    ms = time_stream(torch, call, steps)
+    return ms / steps
+
+
+def cpu_baseline(p, sample_tokens: int):
+    """The oracle as it stands, on the first `sample_tokens` tokens of the
+    prefill workload (all heads), threaded over (b, h) on the host cores."""
+    import oracle
+    cores = max(1, min(os.cpu_count() or 1, 64))
+    inp = gi.make_prefill(p, 0, T=sample_tokens)
+    t0 = time.perf_counter()
+    oracle.gdn_sequential(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["beta"], inp["h0"],
+                          nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": round(p.B * sample_tokens / dt, 3), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"first {sample_tokens} of {p.T} tokens of {p.name}, all {p.Hv} value heads, "
+                      f"fp64 token-serial oracle, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="restrict to one half (profiling runs); 'copy' runs only the plain "
+                         "copy kernel used to calibrate HBM byte counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the gated-delta-rule core shards by heads or "
+              "sequences with no exchange, so a multi-GPU figure is not produced here "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_recurrence_04_amd as gdn
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    p = gi.QWEN27B_PREFILL
+    d = gi.QWEN27B_DECODE
+
+    if args.only == "copy":
+        # a plain device copy of known size: FETCH_SIZE / WRITE_SIZE of this
+        # kernel calibrate the counters of the gated-delta-rule kernels
+        n = 256 * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "launches": max(args.steps, 1)}), flush=True)
+        return
+
+    result = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1,
+              "steps": args.steps, "warmup": args.warmup, "ms_per_step": None,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "bf16 storage, fp32 accumulate/state",
+              "data": "synthetic (seeded numpy PCG64, shapes and distributions of the workload)",
+              "config": {"workload": p.name, "B": p.B, "T": p.T, "Hk": p.Hk, "Hv": p.Hv,
+                         "dk": p.dk, "dv": p.dv, "chunk": p.chunk,
+                         "gate": "log g = -exp(A_log) softplus(dt)", "h0": "N(0, 0.02)"}}
+
+    if args.only in ("all", "prefill"):
+        ms, prob = bench_prefill(torch, gdn, p, args.steps, args.warmup)
+        flops = prefill_useful_flops(p)
+        nbytes = prefill_bytes(p)
+        kernel = gdn.selected_prefill_kernel(prob)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        tflops = flops / (ms * 1e-3) / 1e12
+        src = source_hash(*kernel["sources"])
+        result["value"] = round(p.B * p.T / (ms * 1e-3), 1)
+        result["ms_per_step"] = round(ms, 4)
+        mm_peak = MFMA_BF16_PEAK_TFLOPS if kernel["arith"] == "bf16-mfma" else FP32_VALU_PEAK_TFLOPS
+        hbm_floor = nbytes / (HBM_PEAK_GBPS * 1e9)
+        mm_floor = flops / (mm_peak * 1e12)
+        traffic = pmc_traffic(kernel["name"], src)
+        result["roofline"] = {
+            "bound": "hbm" if hbm_floor >= mm_floor else "mfma",
+            "kernel": kernel["name"],
+            "achieved": round(gbps if hbm_floor >= mm_floor else tflops, 3),
+            "peak": HBM_PEAK_GBPS if hbm_floor >= mm_floor else mm_peak,
+            "unit": "GB/s" if hbm_floor >= mm_floor else "TFLOP/s",
+            "frac": round((gbps / HBM_PEAK_GBPS) if hbm_floor >= mm_floor else (tflops / mm_peak), 5),
+            "traffic": traffic,
+            "algorithmic_bytes": nbytes, "useful_flops": flops,
+            "compute": {"achieved_tflops": round(tflops, 3), "peak_tflops": mm_peak,
+                        "peak_kind": kernel["arith"], "frac": round(tflops / mm_peak, 5),
+                        "frac_of_bf16_mfma": round(tflops / MFMA_BF16_PEAK_TFLOPS, 5)},
+            "avg_launch_us": round(ms * 1e3, 2), "source_hash": src,
+        }
+        log(f"prefill: {ms:.3f} ms/call, {result['value']:.0f} tok/s, {gbps:.1f} GB/s, {tflops:.2f} TFLOP/s")
+
+    if args.only in ("all", "decode"):
+        ms_d = bench_decode(torch, gdn, d, args.decode_steps, min(args.warmup, 10) or 1)
+        nb = decode_bytes(d)
+        gbps_d = nb / (ms_d * 1e-3) / 1e9
+        src_d = source_hash("decode.hip")
+        result["decode"] = {
+            "workload": d.name, "steps": args.decode_steps,
+            "us_per_step": round(ms_d * 1e3, 3),
+            "tokens_per_s": round(d.B / (ms_d * 1e-3), 1),
+            "state_update_GBps": round(gbps_d, 2),
+            "roofline": {"bound": "hbm", "kernel": "decode_step_kernel<128,bf16>",
+                         "achieved": round(gbps_d, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps_d / HBM_PEAK_GBPS, 5),
+                         "traffic": pmc_traffic("decode_step_kernel<128,bf16>", src_d),
+                         "algorithmic_bytes": nb, "source_hash": src_d},
+        }
+        log(f"decode: {ms_d * 1e3:.2f} us/step, {gbps_d:.1f} GB/s")
+        if result["value"] is None:
+            result["value"] = result["decode"]["tokens_per_s"]
+            result["unit"] = "tokens/s (decode)"
+            result["ms_per_step"] = round(ms_d, 5)
+
+    if not args.no_cpu_baseline and args.only in ("all", "prefill"):
+        log("cpu baseline: oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(p, args.cpu_sample_tokens)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

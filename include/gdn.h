@@ -143,6 +143,15 @@ gdn_status gdn_decode_step(const gdn_problem* problem,
                            const float* log_g, const float* beta,
                            float* state, void* o, void* hip_stream);
 
+/*
+ * Name of the prefill kernel variant gdn_chunk_prefill launches for this
+ * problem (static storage, never NULL): "generic_f32" (fp32 arithmetic, any
+ * supported shape), "mfma_bf16" (bf16 MFMA path for bf16 inputs, d = 128,
+ * chunk 64), or "invalid" when the problem would be rejected.  Pure query:
+ * enqueues nothing.
+ */
+const char* gdn_chunk_prefill_variant(const gdn_problem* problem);
+
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* gdn_status_string(gdn_status status);
 

@@ -56,6 +56,8 @@ def lib():
     L.gdn_status_string.argtypes = [ctypes.c_int]
     L.gdn_chunk_prefill_workspace_bytes.restype = sz
     L.gdn_chunk_prefill_workspace_bytes.argtypes = [pp]
+    L.gdn_chunk_prefill_variant.restype = ctypes.c_char_p
+    L.gdn_chunk_prefill_variant.argtypes = [pp]
     L.gdn_chunk_prefill.restype = ctypes.c_int
     L.gdn_chunk_prefill.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, vp, vp, sz, vp]
     L.gdn_decode_step.restype = ctypes.c_int
@@ -85,6 +87,25 @@ def make_problem(B, T, Hk, Hv, dk, dv, *, chunk=64, dtype=GDN_DTYPE_BF16, qk_l2n
 
 def gdn_chunk_prefill_workspace_bytes(problem: GdnProblem) -> int:
     return int(lib().gdn_chunk_prefill_workspace_bytes(ctypes.byref(problem)))
+
+
+def gdn_chunk_prefill_variant(problem: GdnProblem) -> str:
+    return lib().gdn_chunk_prefill_variant(ctypes.byref(problem)).decode()
+
+
+# kernel variant -> (kernel symbol, arithmetic, source files under csrc/)
+VARIANTS = {
+    "generic_f32": ("prefill_generic_kernel", "fp32-valu", ("prefill_generic.hip",)),
+    "mfma_bf16": ("prefill_mfma_kernel", "bf16-mfma", ("prefill_mfma.hip",)),
+}
+
+
+def selected_prefill_kernel(problem: GdnProblem) -> dict:
+    v = gdn_chunk_prefill_variant(problem)
+    if v not in VARIANTS:
+        raise ValueError(f"problem rejected ({v})")
+    name, arith, srcs = VARIANTS[v]
+    return {"variant": v, "name": name, "arith": arith, "sources": srcs}
 
 
 # ---------------------------------------------------------------------------

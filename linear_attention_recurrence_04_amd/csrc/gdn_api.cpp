@@ -72,6 +72,11 @@ const char* gdn_status_string(gdn_status s) {
     return "unknown gdn_status";
 }
 
+const char* gdn_chunk_prefill_variant(const gdn_problem* p) {
+    if (check_problem(p, false) != GDN_OK) return "invalid";
+    return "generic_f32";
+}
+
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* p) {
     if (check_problem(p, false) != GDN_OK) return 0;
     return 0;  // the built prefill kernels keep every intermediate on chip
