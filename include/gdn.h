@@ -148,7 +148,8 @@ gdn_status gdn_decode_step(const gdn_problem* problem,
  * problem (static storage, never NULL): "generic_f32" (fp32 arithmetic, any
  * supported shape), "mfma_bf16" (bf16 MFMA path for bf16 inputs, d = 128,
  * chunk 64), or "invalid" when the problem would be rejected.  Pure query:
- * enqueues nothing.
+ * enqueues nothing.  Setting GDN_FORCE_GENERIC=1 in the environment makes
+ * every prefill use "generic_f32" (for A/B comparisons of the two kernels).
  */
 const char* gdn_chunk_prefill_variant(const gdn_problem* problem);
 

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "gdn.h"
@@ -52,6 +53,25 @@ gdn_status check_problem(const gdn_problem* p, bool decode) {
 
 size_t dsize(const gdn_problem* p) { return p->dtype == GDN_DTYPE_BF16 ? 2 : 4; }
 
+gdn::PrefillArgs prefill_args(const gdn_problem* p) {
+    gdn::PrefillArgs a = {};
+    a.B = p->B; a.T = p->T; a.Hk = p->Hk; a.Hv = p->Hv; a.D = p->dk;
+    a.C = p->chunk ? p->chunk : 64;
+    a.bf16 = p->dtype == GDN_DTYPE_BF16;
+    a.l2norm = p->qk_l2norm;
+    a.q_scale = p->q_scale;
+    return a;
+}
+
+// GDN_FORCE_GENERIC=1 in the environment routes every prefill to the fp32
+// kernel (A/B comparisons between the two kernels on the same problem).
+bool force_generic() {
+    const char* e = getenv("GDN_FORCE_GENERIC");
+    return e && e[0] == '1';
+}
+
+bool use_mfma(const gdn::PrefillArgs& a) { return !force_generic() && gdn::prefill_mfma_supported(a); }
+
 }  // namespace
 
 extern "C" {
@@ -74,7 +94,7 @@ const char* gdn_status_string(gdn_status s) {
 
 const char* gdn_chunk_prefill_variant(const gdn_problem* p) {
     if (check_problem(p, false) != GDN_OK) return "invalid";
-    return "generic_f32";
+    return use_mfma(prefill_args(p)) ? "mfma_bf16" : "generic_f32";
 }
 
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* p) {
@@ -124,15 +144,10 @@ gdn_status gdn_chunk_prefill(const gdn_problem* p, const void* q, const void* k,
         err = gdn::launch_state_copy(h0, hT, s_bytes / sizeof(float), stream);
         return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
     }
-    gdn::PrefillArgs a;
-    a.B = p->B; a.T = p->T; a.Hk = p->Hk; a.Hv = p->Hv; a.D = p->dk;
-    a.C = p->chunk ? p->chunk : 64;
-    a.bf16 = p->dtype == GDN_DTYPE_BF16;
-    a.l2norm = p->qk_l2norm;
-    a.q_scale = p->q_scale;
+    gdn::PrefillArgs a = prefill_args(p);
     a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
     a.h0 = h0; a.hT = hT; a.o = o; a.ws = workspace; a.ws_bytes = workspace_bytes;
-    err = gdn::launch_prefill_generic(a, stream);
+    err = use_mfma(a) ? gdn::launch_prefill_mfma(a, stream) : gdn::launch_prefill_generic(a, stream);
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

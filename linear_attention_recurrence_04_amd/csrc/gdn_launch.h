@@ -37,6 +37,10 @@ hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
 // Portable path: any supported (D, C, dtype); fp32 arithmetic throughout.
 hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t stream);
 
+// bf16 MFMA path: bf16 inputs, head dim 128, chunk 64.
+bool prefill_mfma_supported(const PrefillArgs& a);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
+
 // hT = h0 (or zeros) without touching anything else (T == 0).
 hipError_t launch_state_copy(const float* h0, float* hT, size_t n, hipStream_t stream);
 
