@@ -96,7 +96,7 @@ def gdn_chunk_prefill_variant(problem: GdnProblem) -> str:
 # kernel variant -> (kernel symbol, arithmetic, source files under csrc/)
 VARIANTS = {
     "generic_f32": ("prefill_generic_kernel", "fp32-valu", ("prefill_generic.hip",)),
-    "mfma_bf16": ("prefill_mfma_kernel", "bf16-mfma", ("prefill_mfma.hip",)),
+    "mfma_bf16": ("chunk_prep_kernel+chunk_scan_kernel", "bf16-mfma", ("prefill_mfma.hip",)),
 }
 
 

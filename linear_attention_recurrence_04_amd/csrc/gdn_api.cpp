@@ -99,7 +99,9 @@ const char* gdn_chunk_prefill_variant(const gdn_problem* p) {
 
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* p) {
     if (check_problem(p, false) != GDN_OK) return 0;
-    return 0;  // the built prefill kernels keep every intermediate on chip
+    const gdn::PrefillArgs a = prefill_args(p);
+    if (use_mfma(a)) return gdn::prefill_mfma_workspace_bytes(a.B, a.T, a.Hk, a.Hv);
+    return 0;  // the fp32 kernel keeps every intermediate on chip
 }
 
 gdn_status gdn_chunk_prefill(const gdn_problem* p, const void* q, const void* k, const void* v,

@@ -37,8 +37,11 @@ hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
 // Portable path: any supported (D, C, dtype); fp32 arithmetic throughout.
 hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t stream);
 
-// bf16 MFMA path: bf16 inputs, head dim 128, chunk 64.
+// bf16 MFMA path: bf16 inputs, head dim 128, chunk 64.  Two kernels (a
+// parallel per-chunk prep writing T, P and gates to the workspace, then the
+// serial scan over chunks).
 bool prefill_mfma_supported(const PrefillArgs& a);
+size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
 
 // hT = h0 (or zeros) without touching anything else (T == 0).

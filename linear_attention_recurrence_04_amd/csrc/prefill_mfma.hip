@@ -1,34 +1,39 @@
 // prefill_mfma.hip -- chunked gated-delta-rule prefill on bf16 MFMA (gfx950).
 //
-// Shape: head dim 128, chunk 64, bf16 q/k/v/o, fp32 gates and state.
+// Shape: head dim 128, chunk C = 64, bf16 q/k/v/o, fp32 gates and state.
 //
-// Per value head and chunk of C = 64 tokens starting from state S (128 x dv):
-//   gamma_r = sum_{s<=r} log g_s (in-chunk), Gamma_r = exp(gamma_r),
-//   rk_r, rq_r = 1 / max(|k_r|, 1e-6), 1 / max(|q_r|, 1e-6) (L2 normalisation),
-//   A_rs = beta_r exp(gamma_r - gamma_s) rk_r rk_s (k_r . k_s)   s <  r   decay-masked beta K K^T
-//   P_rs = exp(gamma_r - gamma_s) rq_r rk_s (q_r . k_s)           s <= r
-//   X    = diag(beta) (V - diag(Gamma rk) K S)                   right-hand side
-//   (I + A) Delta = X                                             direct solve
-//   O    = diag(Gamma rq) Q S + P Delta
-//   S'   = Gamma_C S + K^T diag(exp(gamma_C - gamma) rk) Delta
-// This is the token recurrence of "Qwen3.5 Gated Delta Net NKI Kernel for AWS
-// Neuron" ("How It Works") unrolled over a chunk.  The unit lower-triangular
-// system is solved directly -- forward substitution inside 16x16 diagonal
-// blocks, then block forward substitution with MFMA -- never with the Neumann
-// power series ("Qwen3.6: Fused DeltaNet Direct-Solve Follow-Up", "Why This
-// Exists", "Implementation Details").  Only exp(gamma_r - gamma_s) with s <= r
-// is formed, so nothing overflows for log g <= 0.
+// Per value head and chunk (gamma_r = sum_{s<=r} log g_s inside the chunk,
+// Gamma_r = exp(gamma_r), rk/rq = 1 / max(|k|, 1e-6) / 1 / max(|q|, 1e-6)):
+//   A_rs  = beta_r exp(gamma_r - gamma_s) rk_r rk_s (k_r . k_s)   s <  r   decay-masked beta K K^T
+//   P_rs  = exp(gamma_r - gamma_s) rq_r rk_s (q_r . k_s)           s <= r
+//   T     = (I + A)^-1                                             direct triangular solve
+//   X     = diag(beta) (V - diag(Gamma rk) K S)
+//   Delta = T X
+//   O     = diag(Gamma rq) Q S + P Delta
+//   S'    = Gamma_C S + K^T diag(exp(gamma_C - gamma) rk) Delta
+// which is the token recurrence of "Qwen3.5 Gated Delta Net NKI Kernel for
+// AWS Neuron" ("How It Works") unrolled over a chunk.  T is obtained by
+// forward substitution -- inside the 16x16 diagonal blocks in fp32, then block
+// by block with MFMA -- never by the Neumann power series ("Qwen3.6: Fused
+// DeltaNet Direct-Solve Follow-Up", "Why This Exists", "Implementation
+// Details").  Only exp(gamma_r - gamma_s) with s <= r is formed, so nothing
+// overflows for log g <= 0.
 //
-// Mapping: one workgroup (4 waves) per (b, value head, 32-column block of the
-// state).  Columns of the state are independent, so blocks never communicate.
-// The fp32 state block lives in MFMA accumulator layout in registers for the
-// whole sequence (wave w owns rows 32w..32w+31); it is read from h0 once and
-// written to hT once.  Chunk data is staged in LDS with padded rows so that the
-// 16-byte operand reads of 16 lanes hit distinct banks.  Raw bf16 q and k are
-// the MFMA operands (exact); the normalisation scales are applied in fp32 to
-// products, so the only bf16 roundings are of S, X, Delta, A, P and the 16x16
-// inverses used as operands.  Workgroups sharing a key head are placed on one
-// XCD so their repeated q/k chunk reads hit the same L2.
+// Two kernels:
+//  * chunk_prep_kernel -- everything that does not depend on the state, for
+//    all chunks and heads at once (one workgroup per (b, value head, chunk)):
+//    row norms, the two Gram products (MFMA), gates, A, the triangular inverse
+//    T, and P.  T, P and the gate vectors go to the caller's workspace, T and P
+//    already in MFMA operand order.
+//  * chunk_scan_kernel -- the serial chain over chunks.  One workgroup per
+//    (b, value head, 64 state columns); each wave owns a 16-column strip of
+//    the fp32 state for all 128 rows, in MFMA accumulator layout, for the whole
+//    sequence.  Per chunk a wave computes K S and Q S, X, Delta = T X, the
+//    output and the state update in its own registers: a pair of accumulator
+//    tiles is, element for element, a valid operand of the next product once
+//    the contraction index of the other operand is stored in the matching
+//    order (kperm below), so the chain needs no barrier and no LDS round trip.
+//    Chunk inputs are staged in LDS once per workgroup.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -39,29 +44,31 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-constexpr int D = 128;   // head dim (dk = dv)
-constexpr int C = 64;    // chunk
-constexpr int BV = 32;   // state columns per workgroup
-constexpr int NT = 256;  // threads
-constexpr int SK = D + 8;   // padded row stride (elements) of [C][D] bf16 arrays
-constexpr int SC = C + 8;   // padded row stride of [*][C] bf16 arrays
-constexpr int ST = 20;      // row stride of the 16x16 bf16 inverses
+constexpr int D = 128;      // head dim (dk = dv)
+constexpr int C = 64;       // chunk
+constexpr int NT = 256;     // threads per workgroup (both kernels)
+constexpr int SK = D + 8;   // padded row stride (elements) of [64][128] bf16 tiles
+constexpr int SC = C + 8;   // padded row stride of [*][64] bf16 tiles
 
-struct Smem {
-    uint16_t Kr[C][SK];      // raw k rows of the chunk (bf16)
-    uint16_t Qr[C][SK];      // raw q rows
-    uint16_t Kt[D][SC];      // k transposed: [i][s]
-    uint16_t Vt[BV][SC];     // v block transposed: [j][s]
-    uint16_t Sbt[BV][SK];    // state block transposed, bf16: [j][i]
-    uint16_t An[C][SC];      // -A (bf16) [r][s]
-    uint16_t Pb[C][SC];      // P (bf16) [r][s]
-    uint16_t Dt[BV][SC];     // Delta^T (bf16) [j][s]
-    uint16_t Dw[BV][SC];     // (exp(gamma_C - gamma) rk Delta)^T (bf16) [j][s]
-    uint16_t Tb[4][16][ST];  // (I + A_ii)^-1 (bf16), diagonal blocks
-    float Af[4][16][17];     // A_ii (fp32), diagonal blocks
-    float rk[C], rq[C], bt[C], gam[C], Gm[C], Wd[C];
-    float lgn[2][C], btn[2][C];  // gates of the current / next chunk
-};
+// Workspace record per (b, value head, chunk): T and P (64x64 bf16, operand
+// order) and the gate vectors (fp32): grk, wrk, grq, beta, Gamma_C.
+constexpr int WS_T = 0;
+constexpr int WS_P = C * C * 2;
+constexpr int WS_G = 2 * C * C * 2;
+constexpr int NGATE = 5;
+constexpr int WS_REC = WS_G + NGATE * C * 4;   // 17664 bytes
+// After all records: K^T per (b, key head, chunk), [128][64] bf16 with s in
+// operand order (written by the first value head of each key head).
+constexpr int WS_KT = D * C * 2;               // 16384 bytes
+
+// Contraction-index order inside each 32-wide k step.  A pair of accumulator
+// tiles (rows 32ks.., 32ks+16..) gives lane (g, n) the rows {4g..4g+3} and
+// {16+4g..16+4g+3}; a 16x16x32 operand gives lane (g, n) the logical
+// k = 8g..8g+7.  Storing the other operand's physical 4-group q
+// (k = 4q..4q+3) at logical offset kperm(q) makes the two agree.
+__host__ __device__ constexpr int kperm(int q) { return 8 * (q & 3) + 4 * (q >> 2); }
+// logical position of physical index p
+__device__ __forceinline__ int lpos(int p) { return (p & ~31) + kperm((p >> 2) & 7) + (p & 3); }
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -77,364 +84,544 @@ __device__ __forceinline__ s16x4 pack4(f32x4 v) {
     r[0] = bfbits(v[0]); r[1] = bfbits(v[1]); r[2] = bfbits(v[2]); r[3] = bfbits(v[3]);
     return r;
 }
-__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
-    return *reinterpret_cast<const bf16x8*>(p);
+// operand from an accumulator tile pair (lo = rows 4g.., hi = rows 16+4g..)
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
+    bf16x8 r;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        r[t] = static_cast<__bf16>(lo[t]);
+        r[4 + t] = static_cast<__bf16>(hi[t]);
+    }
+    return r;
 }
-__device__ __forceinline__ s16x4 ld4(const uint16_t* p) {
-    return *reinterpret_cast<const s16x4*>(p);
-}
-__device__ __forceinline__ void st4(uint16_t* p, s16x4 v) {
-    *reinterpret_cast<s16x4*>(p) = v;
-}
-
-// x if keep, else zero (component-wise, no control flow)
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ s16x4 ld4(const uint16_t* p) { return *reinterpret_cast<const s16x4*>(p); }
 __device__ __forceinline__ uint4 mask4(uint4 x, bool keep) {
     const uint32_t m = keep ? 0xffffffffu : 0u;
     return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
 }
+// exp(x) through the hardware base-2 exponential (arguments here are <= 0)
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
-// Lower-triangular 16x16 tiles of a 64x64 matrix, in an order the waves split.
+// Lower-triangular 16x16 tiles of a 64x64 matrix: (0,0) (1,0) (1,1) (2,0) ...
 __device__ __forceinline__ void tile_of(int idx, int& a, int& b) {
-    // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
     a = (idx >= 1) + (idx >= 3) + (idx >= 6);
     b = idx - (a * (a + 1)) / 2;
 }
 
-__global__ __launch_bounds__(NT) void prefill_mfma_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+// Order of the contraction index for the transposed k: logical s = 8 blk + x
+// (x = 0..7) is physical s = ksb(blk) + 16 (x >> 2) + (x & 3).
+__device__ __forceinline__ int ksb(int blk) { return 32 * (blk >> 2) + 4 * (blk & 3); }
+
+// ===========================================================================
+// prep: one workgroup per (b, value head h, chunk)
+// ===========================================================================
+
+struct PrepSmem {
+    uint16_t Kr[C][SK];       // raw k rows (bf16)
+    uint16_t Qr[C][SK];       // raw q rows
+    uint16_t Ab[C][SC];       // A (bf16), physical order, off-diagonal blocks
+    uint16_t Tl[C][SC];       // T (bf16), physical order
+    float Af[4][16][17];      // A diagonal blocks (fp32)
+    float rk[C], rq[C], bt[C], gam[C];
+};
+
+__global__ __launch_bounds__(NT) void chunk_prep_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const float* __restrict__ log_g, const float* __restrict__ beta,
-    const float* h0, float* hT, bf16_t* __restrict__ o,
-    int T, int Hk, int Hv, int l2norm, float q_scale, int xcd_remap) {
-    __shared__ Smem sm;
+    unsigned char* __restrict__ ws, unsigned char* __restrict__ ws_kt,
+    int T, int NTc, int Hk, int Hv, int l2norm) {
+    __shared__ PrepSmem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    const int g = lane >> 4;    // lane group (0..3)
-    const int n = lane & 15;    // lane column in a 16-wide tile
+    const int g = lane >> 4;
+    const int n = lane & 15;
+
+    const int chunk = blockIdx.x % NTc;
+    const int bh = blockIdx.x / NTc;
+    const int b = bh / Hv;
+    const int h = bh - b * Hv;
+    const int hk = h / (Hv / Hk);
+    const int t0 = chunk * C;
+    const int L = min(C, T - t0);
+    unsigned char* rec = ws + (size_t)blockIdx.x * WS_REC;
+
+    // ---- stage raw q, k rows (rows >= L are zero); zero the upper blocks of T
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int seg = tid + NT * u;
+        const int r = seg >> 4;
+        const int c8 = (seg & 15) * 8;
+        const size_t off = (((size_t)b * T + t0 + min(r, L - 1)) * Hk + hk) * D + c8;
+        const uint4 kv = *reinterpret_cast<const uint4*>(k + off);
+        const uint4 qv = *reinterpret_cast<const uint4*>(q + off);
+        *reinterpret_cast<uint4*>(&sm.Kr[r][c8]) = mask4(kv, r < L);
+        *reinterpret_cast<uint4*>(&sm.Qr[r][c8]) = mask4(qv, r < L);
+    }
+    for (int e = tid; e < C * C; e += NT) {
+        const int r = e >> 6, s = e & 63;
+        if ((s >> 4) > (r >> 4)) sm.Tl[r][s] = 0;
+    }
+    float lg = 0.f, btv = 0.f;
+    if (w == 0) {   // padding rows: g = 1, beta = 0
+        const size_t gi = ((size_t)b * T + t0 + min(lane, L - 1)) * Hv + h;
+        const float lgr = log_g[gi], btr = beta[gi];
+        lg = (lane < L) ? lgr : 0.f;
+        btv = (lane < L) ? btr : 0.f;
+    }
+    __syncthreads();
+
+    // ---- row norms (4 threads per row); in-chunk decay scan (wave 0)
+    {
+        const int r = tid >> 2;
+        const int p = tid & 3;
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const uint4 kk = *reinterpret_cast<const uint4*>(&sm.Kr[r][32 * p + 8 * x]);
+            const uint4 qq = *reinterpret_cast<const uint4*>(&sm.Qr[r][32 * p + 8 * x]);
+            const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+            const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xffff0000u);
+                const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xffff0000u);
+                sk += k0 * k0 + k1 * k1;
+                sq += q0 * q0 + q1 * q1;
+            }
+        }
+        sk = group_sum<4>(sk);
+        sq = group_sum<4>(sq);
+        if (p == 0) {
+            sm.rk[r] = l2norm ? inv_l2(sk) : 1.f;
+            sm.rq[r] = l2norm ? inv_l2(sq) : 1.f;
+        }
+    }
+    float gam_l = 0.f;
+    if (w == 0) {
+        float x = lg;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            const float y = __shfl_up(x, m, 64);
+            if (lane >= m) x += y;
+        }
+        gam_l = x;
+        sm.gam[lane] = x;
+        sm.bt[lane] = btv;
+    }
+    __syncthreads();
+
+    // ---- gates (wave 0): Gamma rk, exp(gamma_C - gamma) rk, Gamma rq, beta, Gamma_C
+    if (w == 0) {
+        const float total = __shfl(gam_l, 63, 64);
+        const float Gm = exp_hw(gam_l);
+        const float rkv = sm.rk[lane];
+        float* gp = reinterpret_cast<float*>(rec + WS_G);
+        gp[0 * C + lane] = Gm * rkv;
+        gp[1 * C + lane] = exp_hw(total - gam_l) * rkv;
+        gp[2 * C + lane] = Gm * sm.rq[lane];
+        gp[3 * C + lane] = btv;
+        gp[4 * C + lane] = exp_hw(total);
+    }
+
+    // ---- Gram tiles, computed transposed (s on the M side): 10 of K K^T -> A,
+    //      10 of Q K^T -> P.  Lane (g, n) ends with s = 16bb + 4g + t, r = 16a + n.
+    uint16_t* Pg = reinterpret_cast<uint16_t*>(rec + WS_P);
+#pragma unroll 1
+    for (int task = w; task < 20; task += 4) {
+        const bool is_qk = task >= 10;
+        int a, bb;
+        tile_of(is_qk ? task - 10 : task, a, bb);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const uint16_t* rowsB = is_qk ? &sm.Qr[16 * a + n][0] : &sm.Kr[16 * a + n][0];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            acc = mfma32(ld8(&sm.Kr[16 * bb + n][32 * ks + 8 * g]), ld8(rowsB + 32 * ks + 8 * g), acc);
+        const int r = 16 * a + n;
+        const float gr = sm.gam[r];
+        const float sr = is_qk ? sm.rq[r] : sm.rk[r] * sm.bt[r];
+        f32x4 val;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int s = 16 * bb + 4 * g + t;
+            const bool keep = is_qk ? (s <= r) : (s < r);
+            val[t] = keep ? exp_hw(gr - sm.gam[s]) * sr * sm.rk[s] * acc[t] : 0.f;
+        }
+        const int q4 = 4 * bb + g;   // physical 4-group of s
+        if (is_qk) {
+            *reinterpret_cast<s16x4*>(Pg + r * C + 32 * (q4 >> 3) + kperm(q4 & 7)) = pack4(val);
+            if (a == bb && (a == 0 || a == 2)) {  // upper neighbour read by the scan: zero
+                const int qz = q4 + 4;
+                const s16x4 z = {0, 0, 0, 0};
+                *reinterpret_cast<s16x4*>(Pg + r * C + 32 * (qz >> 3) + kperm(qz & 7)) = z;
+            }
+        } else if (a == bb) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sm.Af[a][n][4 * g + t] = val[t];
+        } else {
+            *reinterpret_cast<s16x4*>(&sm.Ab[r][16 * bb + 4 * g]) = pack4(val);
+        }
+    }
+    __syncthreads();
+
+    // ---- diagonal blocks: T_ww = (I + A_ww)^-1 by forward substitution (lane = column)
+    if (lane < 16) {
+        float tc[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == n) ? 1.f : 0.f;
+#pragma unroll
+            for (int s = 0; s < r; ++s) acc -= sm.Af[w][r][s] * tc[s];
+            tc[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.Tl[16 * w + r][16 * w + n] = static_cast<uint16_t>(bfbits(tc[r]));
+    }
+    __syncthreads();
+
+    // ---- off-diagonal blocks of column block j = w:
+    //      (I + A_ii) T_ij + sum_{k=j}^{i-1} A_ik T_kj = 0  =>  T_ij = -T_ii sum_k A_ik T_kj
+    {
+        const int j = w;
+        s16x4 tk[4];   // T_kj as operand (accumulator layout), k = j..3
+        {
+            s16x4 d;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) d[t] = static_cast<short>(sm.Tl[16 * j + 4 * g + t][16 * j + n]);
+            tk[0] = d;
+        }
+#pragma unroll
+        for (int di = 1; di < 4; ++di) {
+            const int i = j + di;
+            if (i < 4) {
+                f32x4 R = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int dk = 0; dk < di; ++dk)
+                    R = mfma16(ld4(&sm.Ab[16 * i + n][16 * (j + dk) + 4 * g]), tk[dk], R);
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 Tij = mfma16(ld4(&sm.Tl[16 * i + n][16 * i + 4 * g]), pack4(-R), zero);
+                tk[di] = pack4(Tij);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    sm.Tl[16 * i + 4 * g + t][16 * j + n] = static_cast<uint16_t>(tk[di][t]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- K^T (operand order in s) once per key head and chunk
+    if (h % (Hv / Hk) == 0) {
+        uint16_t* Kt = reinterpret_cast<uint16_t*>(ws_kt + (((size_t)b * Hk + hk) * NTc + chunk) * WS_KT);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int task = tid + NT * u;
+            const int i = task & (D - 1);
+            const int blk = task >> 7;
+            const int sb = ksb(blk);
+            uint32_t wd[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int s0 = sb + 16 * (x >> 1) + 2 * (x & 1);
+                wd[x] = static_cast<uint32_t>(sm.Kr[s0][i]) | (static_cast<uint32_t>(sm.Kr[s0 + 1][i]) << 16);
+            }
+            *reinterpret_cast<uint4*>(Kt + i * C + 8 * blk) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        }
+    }
+
+    // ---- T to the workspace in operand order (8-byte groups, permuted per 32)
+    uint16_t* Tg = reinterpret_cast<uint16_t*>(rec + WS_T);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int e = tid + NT * u;        // 1024 groups: row r, physical group Qg (16 per row)
+        const int r = e >> 4;
+        const int Qg = e & 15;
+        *reinterpret_cast<uint2*>(Tg + r * C + 32 * (Qg >> 3) + kperm(Qg & 7)) =
+            *reinterpret_cast<const uint2*>(&sm.Tl[r][4 * Qg]);
+    }
+}
+
+// ===========================================================================
+// scan: one workgroup per (b, value head h, 64 state columns); 4 state waves
+// ===========================================================================
+
+constexpr int SW = 16;            // state columns per wave
+constexpr int BVS = 4 * SW;       // state columns per workgroup
+
+struct ScanSmem {
+    uint16_t Kp[C][SK];      // k rows, columns in operand order
+    uint16_t Qp[C][SK];      // q rows, columns in operand order
+    uint16_t Ktp[D][SC];     // k transposed [i][s], s in operand order
+    uint16_t Vr[C][SC];      // v block rows [s][j] (physical)
+    uint16_t Tp[C][SC];      // T, operand order
+    uint16_t Pp[C][SC];      // P, operand order
+    uint16_t Os[C][SC];      // output block of the previous chunk (bf16)
+    float gate[NGATE][C];
+};
+
+__global__ __launch_bounds__(NT) void chunk_scan_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const unsigned char* __restrict__ ws, const unsigned char* __restrict__ ws_kt,
+    const float* h0, float* hT, bf16_t* __restrict__ o,
+    int T, int NTc, int Hk, int Hv, float q_scale, int xcd_remap) {
+    __shared__ ScanSmem sm;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int g = lane >> 4;
+    const int n = lane & 15;
 
     int lid = blockIdx.x;
     if (xcd_remap) {  // consecutive logical ids on one XCD (dispatch is round-robin over 8)
         const int per = gridDim.x >> 3;
         lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     }
-    const int bh = lid >> 2;
-    const int j0 = (lid & 3) * BV;
+    const int bh = lid >> 1;
+    const int j0 = (lid & 1) * BVS;
+    const int jw = j0 + SW * w;          // this wave's first state column
     const int b = bh / Hv;
     const int h = bh - b * Hv;
     const int hk = h / (Hv / Hk);
     const size_t state_base = (size_t)bh * D * D;
+    const unsigned char* rec0 = ws + (size_t)bh * NTc * WS_REC;
+    const unsigned char* kt0 = ws_kt + ((size_t)b * Hk + hk) * NTc * WS_KT;
+    // chunk-invariant parts of the addresses (elements)
+    const bf16_t* kbase = k + ((size_t)b * T * Hk + hk) * D;
+    const bf16_t* qbase = q + ((size_t)b * T * Hk + hk) * D;
+    const bf16_t* vbase = v + ((size_t)b * T * Hv + h) * D + j0;
+    bf16_t* obase = o + ((size_t)b * T * Hv + h) * D + j0;
+    const int rowk = Hk * D;             // element stride between tokens of q and k
+    const int rowv = Hv * D;             // element stride between tokens of v and o
 
-    // ---- state block in accumulator layout: tile (a, c) holds rows
-    //      32w + 16a + 4g + t and columns j0 + 16c + n
-    f32x4 S[2][2];
+    // state strip: tile a holds rows 16a + 4g + t, column jw + n
+    f32x4 S[8];
+    if (h0) {
+        const float* hp = h0 + state_base + jw + n;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+            for (int t = 0; t < 4; ++t) S[a][t] = hp[(16 * a + 4 * g + t) * D];
+    } else {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                S[a][c][t] = h0 ? h0[state_base + (size_t)(32 * w + 16 * a + 4 * g + t) * D + j0 + 16 * c + n]
-                                : 0.f;
+        for (int a = 0; a < 8; ++a) S[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-    // ---- prefetch registers for one chunk
-    uint4 pk[4], pq[4], pv;
-    float plg = 0.f, pbt = 0.f;
-    // Loads are branch-free (rows past the end read a clamped valid row and are
-    // zeroed when staged), so no wait is forced right after issuing them.
-    auto prefetch = [&](int t0) {
+    // ---- prefetch registers of one chunk (branch-free: rows past the end
+    //      read a clamped valid row and are zeroed when staged)
+    uint4 pk[4], pq[4], pkt0, pkt1, pkt2, pkt3, pv0, pv1, pt0, pt1, pp0, pp1, pg;
+    auto prefetch = [&](int chunk) __attribute__((always_inline)) {
+        const int t0 = chunk * C;
         const int last = min(C, T - t0) - 1;
+        const bf16_t* kc = kbase + (size_t)t0 * rowk;
+        const bf16_t* qc = qbase + (size_t)t0 * rowk;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int seg = tid + NT * u;       // 0..1023: (row, 8-element column group)
-            const int r = min(seg >> 4, last);
-            const int c8 = (seg & 15) * 8;
-            const size_t off = (((size_t)b * T + t0 + r) * Hk + hk) * D + c8;
-            pk[u] = *reinterpret_cast<const uint4*>(k + off);
-            pq[u] = *reinterpret_cast<const uint4*>(q + off);
+            const int seg = tid + NT * u;
+            const int off = min(seg >> 4, last) * rowk + (seg & 15) * 8;
+            pk[u] = *reinterpret_cast<const uint4*>(kc + off);
+            pq[u] = *reinterpret_cast<const uint4*>(qc + off);
         }
-        {
-            const int r = min(tid >> 2, last);
-            const int c8 = (tid & 3) * 8;
-            pv = *reinterpret_cast<const uint4*>(v + (((size_t)b * T + t0 + r) * Hv + h) * D + j0 + c8);
-        }
-        {
-            const size_t gi = ((size_t)b * T + t0 + min(lane, last)) * Hv + h;
-            plg = log_g[gi];
-            pbt = beta[gi];
+        const bf16_t* vc = vbase + (size_t)t0 * rowv;
+        const int c8 = (tid & 7) * 8;
+        pv0 = *reinterpret_cast<const uint4*>(vc + min(tid >> 3, last) * rowv + c8);
+        pv1 = *reinterpret_cast<const uint4*>(vc + min((tid + NT) >> 3, last) * rowv + c8);
+        const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;
+        pt0 = *reinterpret_cast<const uint4*>(rec + WS_T + 16 * tid);
+        pt1 = *reinterpret_cast<const uint4*>(rec + WS_T + 16 * (tid + NT));
+        pp0 = *reinterpret_cast<const uint4*>(rec + WS_P + 16 * tid);
+        pp1 = *reinterpret_cast<const uint4*>(rec + WS_P + 16 * (tid + NT));
+        pg = *reinterpret_cast<const uint4*>(rec + WS_G + 16 * min(tid, NGATE * C / 4 - 1));
+        const unsigned char* ktc = kt0 + (size_t)chunk * WS_KT + 16 * tid;
+        pkt0 = *reinterpret_cast<const uint4*>(ktc);
+        pkt1 = *reinterpret_cast<const uint4*>(ktc + 16 * NT);
+        pkt2 = *reinterpret_cast<const uint4*>(ktc + 32 * NT);
+        pkt3 = *reinterpret_cast<const uint4*>(ktc + 48 * NT);
+    };
+    // the previous chunk's output, from LDS to HBM in 16-byte rows
+    auto store_out = [&](int chunk) __attribute__((always_inline)) {
+        const int t0 = chunk * C;
+        const int L = min(C, T - t0);
+        bf16_t* oc = obase + (size_t)t0 * rowv;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int seg = tid + NT * u;
+            const int r = seg >> 3;
+            if (r < L)
+                *reinterpret_cast<uint4*>(oc + r * rowv + (seg & 7) * 8) =
+                    *reinterpret_cast<const uint4*>(&sm.Os[r][(seg & 7) * 8]);
         }
     };
 
-    if (T > 0) {
-        prefetch(0);
-        if (w == 0) {
-            sm.lgn[0][lane] = plg;
-            sm.btn[0][lane] = pbt;
-        }
-    }
+    prefetch(0);
 
-    for (int t0 = 0; t0 < T; t0 += C) {
-        const int L = min(C, T - t0);
-        __syncthreads();  // (A) every reader of the previous chunk's LDS is done
+    for (int chunk = 0; chunk < NTc; ++chunk) {
+        const int L = min(C, T - chunk * C);
+        __syncthreads();  // (A) previous chunk's readers of LDS are done
 
-        // ---- stage the chunk in LDS (rows >= L are zero: g = 1, beta = 0, q = k = v = 0)
+        // ---- stage: k, q rows with operand-order columns (8-byte groups); the rest as is
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int seg = tid + NT * u;
             const int r = seg >> 4;
-            const int c8 = (seg & 15) * 8;
-            *reinterpret_cast<uint4*>(&sm.Kr[r][c8]) = mask4(pk[u], r < L);
-            *reinterpret_cast<uint4*>(&sm.Qr[r][c8]) = mask4(pq[u], r < L);
+            const int Q0 = (seg & 15) * 2;   // physical 4-groups Q0, Q0 + 1
+            const uint4 kv = mask4(pk[u], r < L);
+            const uint4 qv = mask4(pq[u], r < L);
+            const int c0 = 32 * (Q0 >> 3) + kperm(Q0 & 7);
+            const int c1 = 32 * ((Q0 + 1) >> 3) + kperm((Q0 + 1) & 7);
+            *reinterpret_cast<uint2*>(&sm.Kp[r][c0]) = make_uint2(kv.x, kv.y);
+            *reinterpret_cast<uint2*>(&sm.Kp[r][c1]) = make_uint2(kv.z, kv.w);
+            *reinterpret_cast<uint2*>(&sm.Qp[r][c0]) = make_uint2(qv.x, qv.y);
+            *reinterpret_cast<uint2*>(&sm.Qp[r][c1]) = make_uint2(qv.z, qv.w);
+        }
+        {   // K^T: segment e holds row e >> 3, logical s (e & 7) * 8 .. + 7
+            const int c8 = (tid & 7) * 8, r0 = tid >> 3;
+            *reinterpret_cast<uint4*>(&sm.Ktp[r0][c8]) = pkt0;
+            *reinterpret_cast<uint4*>(&sm.Ktp[r0 + 32][c8]) = pkt1;
+            *reinterpret_cast<uint4*>(&sm.Ktp[r0 + 64][c8]) = pkt2;
+            *reinterpret_cast<uint4*>(&sm.Ktp[r0 + 96][c8]) = pkt3;
         }
         {
-            const int r = tid >> 2;
-            const int c8 = (tid & 3) * 8;
-            const uint4 vv = mask4(pv, r < L);
-            const uint32_t words[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-            for (int x = 0; x < 8; ++x)
-                sm.Vt[c8 + x][r] = static_cast<uint16_t>(words[x >> 1] >> (16 * (x & 1)));
+            const int r0 = tid >> 3, r1 = (tid + NT) >> 3, c8 = (tid & 7) * 8;
+            *reinterpret_cast<uint4*>(&sm.Vr[r0][c8]) = mask4(pv0, r0 < L);
+            *reinterpret_cast<uint4*>(&sm.Vr[r1][c8]) = mask4(pv1, r1 < L);
+            *reinterpret_cast<uint4*>(&sm.Tp[r0][c8]) = pt0;
+            *reinterpret_cast<uint4*>(&sm.Tp[r1][c8]) = pt1;
+            *reinterpret_cast<uint4*>(&sm.Pp[r0][c8]) = pp0;
+            *reinterpret_cast<uint4*>(&sm.Pp[r1][c8]) = pp1;
         }
-        const int par = (t0 / C) & 1;
-        const float lg_mine = (lane < L) ? sm.lgn[par][lane] : 0.f;
-        const float bt_mine = (lane < L) ? sm.btn[par][lane] : 0.f;
+        if (tid < NGATE * C / 4) *reinterpret_cast<uint4*>(&sm.gate[0][0] + 4 * tid) = pg;
         __syncthreads();  // (B)
 
-        // next chunk's loads overlap everything below
-        if (t0 + C < T) prefetch(t0 + C);
+        // previous output out first, then the next chunk's loads
+        if (chunk > 0) store_out(chunk - 1);
+        if (chunk + 1 < NTc) prefetch(chunk + 1);
 
-        // ---- row norms (4 threads per row) and the in-chunk decay scan (wave 0)
-        {
-            const int r = tid >> 2;
-            const int p = tid & 3;
-            float sk = 0.f, sq = 0.f;
+        // Operands are read from LDS in batches ahead of the MFMAs that use
+        // them (sched_barrier keeps the order): with one wave per SIMD nothing
+        // else would hide the LDS latency.
+        // ---- gate vectors, v values and the K / Q operands of the first k step
+        f32x4 btv[4], grk[4], grq[4];
+        uint32_t vv[4][4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const uint4 kk = *reinterpret_cast<const uint4*>(&sm.Kr[r][32 * p + 8 * x]);
-                const uint4 qq = *reinterpret_cast<const uint4*>(&sm.Qr[r][32 * p + 8 * x]);
-                const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
-                const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+        for (int i = 0; i < 4; ++i) {
+            const int s0 = 16 * i + 4 * g;
+            btv[i] = *reinterpret_cast<const f32x4*>(&sm.gate[3][s0]);
+            grk[i] = *reinterpret_cast<const f32x4*>(&sm.gate[0][s0]);
+            grq[i] = *reinterpret_cast<const f32x4*>(&sm.gate[2][s0]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xffff0000u);
-                    const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xffff0000u);
-                    sk += k0 * k0 + k1 * k1;
-                    sq += q0 * q0 + q1 * q1;
+            for (int t = 0; t < 4; ++t) vv[i][t] = sm.Vr[s0 + t][jw - j0 + n];
+        }
+        bf16x8 SB[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) SB[ks] = pack8(S[2 * ks], S[2 * ks + 1]);
+        f32x4 KS[4], QS[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            KS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            QS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        bf16x8 ak[4], aq[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ak[i] = ld8(&sm.Kp[16 * i + n][8 * g]);
+            aq[i] = ld8(&sm.Qp[16 * i + n][8 * g]);
+        }
+        // ---- K S and Q S: k step outer, 8 independent accumulators inner
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 nk[4], nq[4];
+            if (ks < 3) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    nk[i] = ld8(&sm.Kp[16 * i + n][32 * (ks + 1) + 8 * g]);
+                    nq[i] = ld8(&sm.Qp[16 * i + n][32 * (ks + 1) + 8 * g]);
                 }
             }
-            sk = group_sum<4>(sk);
-            sq = group_sum<4>(sq);
-            if (p == 0) {
-                sm.rk[r] = l2norm ? inv_l2(sk) : 1.f;
-                sm.rq[r] = l2norm ? inv_l2(sq) : 1.f;
-            }
-        }
-        if (w == 0) {
-            float x = lg_mine;
-#pragma unroll
-            for (int m = 1; m < 64; m <<= 1) {
-                const float y = __shfl_up(x, m, 64);
-                if (lane >= m) x += y;
-            }
-            const float total = __shfl(x, 63, 64);
-            sm.gam[lane] = x;
-            sm.Gm[lane] = expf(x);
-            sm.Wd[lane] = expf(total - x);
-            sm.bt[lane] = bt_mine;
-        }
-        __syncthreads();  // (C)
-
-        // ---- Gram tiles: 10 lower tiles of K K^T (-> -A) and 10 of Q K^T (-> P).
-        //      Computed transposed (s on the M side) so each lane ends up with
-        //      four consecutive s of one row r: 8-byte row-major writes.
-#pragma unroll 1
-        for (int task = w; task < 20; task += 4) {
-            const bool is_qk = task >= 10;
-            int a, bb;
-            tile_of(is_qk ? task - 10 : task, a, bb);   // r-block a >= s-block bb
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const uint16_t* rowsB = is_qk ? &sm.Qr[16 * a + n][0] : &sm.Kr[16 * a + n][0];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 av = ld8(&sm.Kr[16 * bb + n][32 * ks + 8 * g]);   // rows s
-                const bf16x8 bv = ld8(rowsB + 32 * ks + 8 * g);               // rows r
-                acc = mfma32(av, bv, acc);
-            }
-            const int r = 16 * a + n;
-            const float gr = sm.gam[r];
-            const float sr = is_qk ? sm.rq[r] : sm.rk[r] * sm.bt[r];
-            float val[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int s = 16 * bb + 4 * g + t;
-                const bool keep = is_qk ? (s <= r) : (s < r);
-                val[t] = keep ? expf(gr - sm.gam[s]) * sr * sm.rk[s] * acc[t] : 0.f;
-            }
-            const int s0 = 16 * bb + 4 * g;
-            if (is_qk) {
-                f32x4 pv4 = {val[0], val[1], val[2], val[3]};
-                st4(&sm.Pb[r][s0], pack4(pv4));
-                if (a == bb && (a == 0 || a == 2)) {  // upper neighbour read by P Delta: zero it
-                    s16x4 z = {0, 0, 0, 0};
-                    st4(&sm.Pb[r][s0 + 16], z);
-                }
-            } else {
-                f32x4 nv = {-val[0], -val[1], -val[2], -val[3]};
-                st4(&sm.An[r][s0], pack4(nv));
-                if (a == bb) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) sm.Af[a][n][4 * g + t] = val[t];
-                }
-            }
-        }
-
-        // ---- k transposed ([i][s], operand of the state update), read from the
-        //      staged rows: 8 two-byte reads of one column, one 16-byte write
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int task = tid + NT * u;
-            const int i = task & (D - 1);
-            const int s8 = (task >> 7) * 8;
-            uint32_t wd[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                wd[x] = static_cast<uint32_t>(sm.Kr[s8 + 2 * x][i]) |
-                        (static_cast<uint32_t>(sm.Kr[s8 + 2 * x + 1][i]) << 16);
-            *reinterpret_cast<uint4*>(&sm.Kt[i][s8]) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-        }
-
-        // ---- state block -> bf16, transposed (operand of K S and Q S)
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-                st4(&sm.Sbt[16 * c + n][32 * w + 16 * a + 4 * g], pack4(S[a][c]));
-        __syncthreads();  // (D)
-
-        // ---- (I + A_ww)^-1 of diagonal block w by forward substitution; lane n = column
-        if (lane < 16) {
-            float tc[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == n) ? 1.f : 0.f;
-#pragma unroll
-                for (int s = 0; s < r; ++s) acc -= sm.Af[w][r][s] * tc[s];
-                tc[r] = acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.Tb[w][r][n] = static_cast<uint16_t>(bfbits(tc[r]));
-        }
-        if (w == 0 && t0 + C < T) {  // gates of the next chunk (loaded by the prefetch)
-            sm.lgn[par ^ 1][lane] = plg;
-            sm.btn[par ^ 1][lane] = pbt;
-        }
-        __syncthreads();  // (E)
-
-        // ---- waves 0,1: X = beta (V - Gamma rk K S), direct block solve -> Delta
-        //      waves 2,3: Gamma rq Q S (first half of the output)
-        const int ct = w & 1;                 // column tile of this wave
-        f32x4 acc4[4];
-        {
-            const uint16_t* Abase = (w < 2) ? &sm.Kr[0][0] : &sm.Qr[0][0];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                acc4[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 av = ld8(Abase + (16 * a + n) * SK + 32 * ks + 8 * g);
-                    const bf16x8 bv = ld8(&sm.Sbt[16 * ct + n][32 * ks + 8 * g]);
-                    acc4[a] = mfma32(av, bv, acc4[a]);
-                }
-            }
-        }
-        if (w < 2) {
-            f32x4 dl[4];
-            s16x4 dlb[4];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                // right-hand side rows 16i + 4g + t, column 16ct + n
-                const s16x4 vv = ld4(&sm.Vt[16 * ct + n][16 * i + 4 * g]);
-                f32x4 rhs;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int s = 16 * i + 4 * g + t;
-                    const float vf = __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(vv[t])) << 16);
-                    rhs[t] = sm.bt[s] * (vf - sm.Gm[s] * sm.rk[s] * acc4[i][t]);
-                }
-                // subtract the solved blocks: rhs += (-A_ij) Delta_j
-#pragma unroll
-                for (int jb = 0; jb < i; ++jb)
-                    rhs = mfma16(ld4(&sm.An[16 * i + n][16 * jb + 4 * g]), dlb[jb], rhs);
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                dl[i] = mfma16(ld4(&sm.Tb[i][n][4 * g]), pack4(rhs), zero);
-                dlb[i] = pack4(dl[i]);
+                KS[i] = mfma32(ak[i], SB[ks], KS[i]);
+                QS[i] = mfma32(aq[i], SB[ks], QS[i]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks < 3) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                st4(&sm.Dt[16 * ct + n][16 * i + 4 * g], dlb[i]);
-                f32x4 sc;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int s = 16 * i + 4 * g + t;
-                    sc[t] = sm.Wd[s] * sm.rk[s] * dl[i][t];
-                }
-                st4(&sm.Dw[16 * ct + n][16 * i + 4 * g], pack4(sc));
-            }
-        } else {
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int r = 16 * a + 4 * g + t;
-                    acc4[a][t] *= sm.Gm[r] * sm.rq[r];
-                }
-        }
-        __syncthreads();  // (F)
-
-        // ---- state update S <- Gamma_C S + K^T Dw (all waves, own rows)
-        {
-            const float GC = sm.Gm[C - 1];
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    f32x4 s4 = S[a][c] * GC;
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        s4 = mfma32(ld8(&sm.Kt[32 * w + 16 * a + n][32 * ks + 8 * g]),
-                                    ld8(&sm.Dw[16 * c + n][32 * ks + 8 * g]), s4);
-                    S[a][c] = s4;
-                }
-        }
-        // ---- waves 2,3: O = Gamma rq Q S + P Delta, stored as bf16
-        if (w >= 2) {
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                f32x4 o4 = acc4[a];
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (ks == 1 && a < 2) continue;   // P is zero there
-                    o4 = mfma32(ld8(&sm.Pb[16 * a + n][32 * ks + 8 * g]),
-                                ld8(&sm.Dt[16 * ct + n][32 * ks + 8 * g]), o4);
-                }
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int r = 16 * a + 4 * g + t;
-                    if (r < L)
-                        o[(((size_t)b * T + t0 + r) * Hv + h) * D + j0 + 16 * ct + n] =
-                            static_cast<uint16_t>(bfbits(q_scale * o4[t]));
+                for (int i = 0; i < 4; ++i) {
+                    ak[i] = nk[i];
+                    aq[i] = nq[i];
                 }
             }
         }
+        // ---- T operands (needed next), issued before the X arithmetic
+        bf16x8 at0[4], at1[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) at0[i] = ld8(&sm.Tp[16 * i + n][8 * g]);
+        at1[0] = ld8(&sm.Tp[32 + n][32 + 8 * g]);
+        at1[1] = ld8(&sm.Tp[48 + n][32 + 8 * g]);
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- X = beta (V - Gamma rk K S)
+        f32x4 X[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                X[i][t] = btv[i][t] * (__uint_as_float(vv[i][t] << 16) - grk[i][t] * KS[i][t]);
+        const bf16x8 XB0 = pack8(X[0], X[1]);
+        const bf16x8 XB1 = pack8(X[2], X[3]);
+        // ---- state-update and output operands, issued before Delta = T X
+        bf16x8 akt[8][2], ap0[4], ap1[2];
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+            akt[a][0] = ld8(&sm.Ktp[16 * a + n][8 * g]);
+            akt[a][1] = ld8(&sm.Ktp[16 * a + n][32 + 8 * g]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ap0[i] = ld8(&sm.Pp[16 * i + n][8 * g]);
+        ap1[0] = ld8(&sm.Pp[32 + n][32 + 8 * g]);
+        ap1[1] = ld8(&sm.Pp[48 + n][32 + 8 * g]);
+        const f32x4 wlo0 = *reinterpret_cast<const f32x4*>(&sm.gate[1][4 * g]);
+        const f32x4 whi0 = *reinterpret_cast<const f32x4*>(&sm.gate[1][16 + 4 * g]);
+        const f32x4 wlo1 = *reinterpret_cast<const f32x4*>(&sm.gate[1][32 + 4 * g]);
+        const f32x4 whi1 = *reinterpret_cast<const f32x4*>(&sm.gate[1][48 + 4 * g]);
+        const float GC = sm.gate[4][0];
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- Delta = T X (T lower triangular: row tile i needs k steps <= i/2)
+        f32x4 Dl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Dl[i] = mfma32(at0[i], XB0, f32x4{0.f, 0.f, 0.f, 0.f});
+        Dl[2] = mfma32(at1[0], XB1, Dl[2]);
+        Dl[3] = mfma32(at1[1], XB1, Dl[3]);
+        // ---- operands of Delta: plain (output) and scaled (state update)
+        const bf16x8 DB0 = pack8(Dl[0], Dl[1]);
+        const bf16x8 DB1 = pack8(Dl[2], Dl[3]);
+        const bf16x8 DWB0 = pack8(Dl[0] * wlo0, Dl[1] * whi0);
+        const bf16x8 DWB1 = pack8(Dl[2] * wlo1, Dl[3] * whi1);
+        // ---- state update S <- Gamma_C S + K^T (wrk Delta), 8 independent tiles
+#pragma unroll
+        for (int a = 0; a < 8; ++a) S[a] = mfma32(akt[a][0], DWB0, S[a] * GC);
+#pragma unroll
+        for (int a = 0; a < 8; ++a) S[a] = mfma32(akt[a][1], DWB1, S[a]);
+        // ---- output O = Gamma rq Q S + P Delta, into LDS (stored next chunk)
+        f32x4 O4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O4[i] = mfma32(ap0[i], DB0, grq[i] * QS[i]);
+        O4[2] = mfma32(ap1[0], DB1, O4[2]);
+        O4[3] = mfma32(ap1[1], DB1, O4[3]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                sm.Os[16 * i + 4 * g + t][SW * w + n] = static_cast<uint16_t>(bfbits(q_scale * O4[i][t]));
     }
+    __syncthreads();
+    store_out(NTc - 1);
 
     if (hT) {
+        float* hp = hT + state_base + jw + n;
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 8; ++a)
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    hT[state_base + (size_t)(32 * w + 16 * a + 4 * g + t) * D + j0 + 16 * c + n] = S[a][c][t];
+            for (int t = 0; t < 4; ++t) hp[(16 * a + 4 * g + t) * D] = S[a][t];
     }
 }
 
@@ -444,14 +631,29 @@ bool prefill_mfma_supported(const PrefillArgs& a) {
     return a.bf16 && a.D == 128 && a.C == 64;
 }
 
+size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv) {
+    const size_t NTc = (size_t)(T + mfma_prefill::C - 1) / mfma_prefill::C;
+    return (size_t)B * Hv * NTc * mfma_prefill::WS_REC + (size_t)B * Hk * NTc * mfma_prefill::WS_KT;
+}
+
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
-    const int blocks = a.B * a.Hv * (128 / mfma_prefill::BV);
-    if (blocks == 0) return hipSuccess;
-    const int remap = (blocks % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(mfma_prefill::prefill_mfma_kernel, dim3(blocks), dim3(mfma_prefill::NT), 0, stream,
+    using namespace mfma_prefill;
+    const int NTc = (a.T + C - 1) / C;
+    const int prep_blocks = a.B * a.Hv * NTc;
+    if (prep_blocks == 0) return hipSuccess;
+    unsigned char* ws = static_cast<unsigned char*>(a.ws);
+    unsigned char* ws_kt = ws + (size_t)a.B * a.Hv * NTc * WS_REC;
+    hipLaunchKernelGGL(chunk_prep_kernel, dim3(prep_blocks), dim3(NT), 0, stream,
+                       static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k), a.log_g, a.beta,
+                       ws, ws_kt, a.T, NTc, a.Hk, a.Hv, a.l2norm);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int scan_blocks = a.B * a.Hv * (D / BVS);
+    const int remap = (scan_blocks % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(chunk_scan_kernel, dim3(scan_blocks), dim3(NT), 0, stream,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
-                       static_cast<const bf16_t*>(a.v), a.log_g, a.beta, a.h0, a.hT,
-                       static_cast<bf16_t*>(a.o), a.T, a.Hk, a.Hv, a.l2norm, a.q_scale, remap);
+                       static_cast<const bf16_t*>(a.v), ws, ws_kt, a.h0, a.hT,
+                       static_cast<bf16_t*>(a.o), a.T, NTc, a.Hk, a.Hv, a.q_scale, remap);
     return hipGetLastError();
 }
 
