@@ -109,6 +109,14 @@ __device__ __forceinline__ void tile_of(int idx, int& a, int& b) {
     b = idx - (a * (a + 1)) / 2;
 }
 
+// The [rows][64] bf16 images (T, P, k transposed) are read by the scan as
+// 16-byte MFMA operands; chunk c (logical columns 8c..8c+7) of row r is stored
+// at chunk c ^ ((r >> 1) & 7), so that the 16 rows an operand read touches
+// hit distinct LDS banks.  Element position of logical column L in row r:
+__host__ __device__ constexpr int img64(int r, int L) {
+    return r * 64 + 8 * ((L >> 3) ^ ((r >> 1) & 7)) + (L & 7);
+}
+
 // Order of the contraction index for the transposed k: logical s = 8 blk + x
 // (x = 0..7) is physical s = ksb(blk) + 16 (x >> 2) + (x & 3).
 __device__ __forceinline__ int ksb(int blk) { return 32 * (blk >> 2) + 4 * (blk & 3); }
@@ -250,11 +258,11 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
         }
         const int q4 = 4 * bb + g;   // physical 4-group of s
         if (is_qk) {
-            *reinterpret_cast<s16x4*>(Pg + r * C + 32 * (q4 >> 3) + kperm(q4 & 7)) = pack4(val);
+            *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (q4 >> 3) + kperm(q4 & 7))) = pack4(val);
             if (a == bb && (a == 0 || a == 2)) {  // upper neighbour read by the scan: zero
                 const int qz = q4 + 4;
                 const s16x4 z = {0, 0, 0, 0};
-                *reinterpret_cast<s16x4*>(Pg + r * C + 32 * (qz >> 3) + kperm(qz & 7)) = z;
+                *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (qz >> 3) + kperm(qz & 7))) = z;
             }
         } else if (a == bb) {
 #pragma unroll
@@ -310,14 +318,17 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     }
     __syncthreads();
 
-    // ---- K^T (operand order in s) once per key head and chunk
+    // ---- K^T once per key head and chunk: image row rho holds k column
+    //      i = lpos(rho) (the scan stores state rows in that order), s in
+    //      operand order, chunks swizzled as in img64
     if (h % (Hv / Hk) == 0) {
         uint16_t* Kt = reinterpret_cast<uint16_t*>(ws_kt + (((size_t)b * Hk + hk) * NTc + chunk) * WS_KT);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int task = tid + NT * u;
-            const int i = task & (D - 1);
-            const int blk = task >> 7;
+            const int rho = task & (D - 1);
+            const int blk = task >> 7;          // logical s = 8 blk .. 8 blk + 7
+            const int i = lpos(rho);
             const int sb = ksb(blk);
             uint32_t wd[4];
 #pragma unroll
@@ -325,7 +336,7 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
                 const int s0 = sb + 16 * (x >> 1) + 2 * (x & 1);
                 wd[x] = static_cast<uint32_t>(sm.Kr[s0][i]) | (static_cast<uint32_t>(sm.Kr[s0 + 1][i]) << 16);
             }
-            *reinterpret_cast<uint4*>(Kt + i * C + 8 * blk) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            *reinterpret_cast<uint4*>(Kt + img64(rho, 8 * blk)) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
         }
     }
 
@@ -336,35 +347,47 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
         const int e = tid + NT * u;        // 1024 groups: row r, physical group Qg (16 per row)
         const int r = e >> 4;
         const int Qg = e & 15;
-        *reinterpret_cast<uint2*>(Tg + r * C + 32 * (Qg >> 3) + kperm(Qg & 7)) =
+        *reinterpret_cast<uint2*>(Tg + img64(r, 32 * (Qg >> 3) + kperm(Qg & 7))) =
             *reinterpret_cast<const uint2*>(&sm.Tl[r][4 * Qg]);
     }
 }
 
 // ===========================================================================
-// scan: one workgroup per (b, value head h, 64 state columns); 4 state waves
+// scan: one workgroup per (b, value head h, 32 state columns): two compute
+// waves (one per 16 columns) and two loader waves that stream the next
+// chunk's inputs into the other LDS buffer and store the previous output
 // ===========================================================================
 
-constexpr int SW = 16;            // state columns per wave
-constexpr int BVS = 4 * SW;       // state columns per workgroup
+constexpr int SW = 16;            // state columns per compute wave
+constexpr int SWAVES = 2;         // compute waves per workgroup
+constexpr int LWAVES = 2;         // loader waves per workgroup (global -> LDS, output stores)
+constexpr int SNT = 64 * (SWAVES + LWAVES);  // threads per workgroup
+constexpr int BVS = SW * SWAVES;  // state columns per workgroup
+constexpr int OS = BVS + 8;       // row stride (elements) of the output staging tile
 
-struct ScanSmem {
-    uint16_t Kp[C][SK];      // k rows, columns in operand order
-    uint16_t Qp[C][SK];      // q rows, columns in operand order
-    uint16_t Ktp[D][SC];     // k transposed [i][s], s in operand order
-    uint16_t Vr[C][SC];      // v block rows [s][j] (physical)
-    uint16_t Tp[C][SC];      // T, operand order
-    uint16_t Pp[C][SC];      // P, operand order
-    uint16_t Os[C][SC];      // output block of the previous chunk (bf16)
-    float gate[NGATE][C];
+// One chunk's inputs, as they arrive by direct global -> LDS loads.
+struct ScanBuf {
+    uint4 K[C * 16];       // k rows: chunk c of row r at c ^ (r & 15)
+    uint4 Q[C * 16];       // q rows, same
+    uint4 Kt[D * 8];       // k transposed image (img64 order)
+    uint4 T[C * 8];        // T image
+    uint4 P[C * 8];        // P image
+    uint4 V[C * 4];        // v block rows: chunk c of row s at c ^ ((s >> 2) & 3)
+    float gate[NGATE * C]; // grk, wrk, grq, beta, Gamma_C
 };
 
-__global__ __launch_bounds__(NT) void chunk_scan_kernel(
+// direct 16-byte load of one lane into LDS at base + 16 * lane (base wave-uniform)
+__device__ __forceinline__ void lds_load16(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
+}
+
+__global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const unsigned char* __restrict__ ws, const unsigned char* __restrict__ ws_kt,
     const float* h0, float* hT, bf16_t* __restrict__ o,
     int T, int NTc, int Hk, int Hv, float q_scale, int xcd_remap) {
-    __shared__ ScanSmem sm;
+    __shared__ ScanBuf buf[2];
+    __shared__ uint16_t Os[2][C][OS];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -376,8 +399,9 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
         const int per = gridDim.x >> 3;
         lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     }
-    const int bh = lid >> 1;
-    const int j0 = (lid & 1) * BVS;
+    constexpr int NB = D / BVS;          // column blocks per head
+    const int bh = lid / NB;
+    const int j0 = (lid % NB) * BVS;
     const int jw = j0 + SW * w;          // this wave's first state column
     const int b = bh / Hv;
     const int h = bh - b * Hv;
@@ -385,7 +409,6 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
     const size_t state_base = (size_t)bh * D * D;
     const unsigned char* rec0 = ws + (size_t)bh * NTc * WS_REC;
     const unsigned char* kt0 = ws_kt + ((size_t)b * Hk + hk) * NTc * WS_KT;
-    // chunk-invariant parts of the addresses (elements)
     const bf16_t* kbase = k + ((size_t)b * T * Hk + hk) * D;
     const bf16_t* qbase = q + ((size_t)b * T * Hk + hk) * D;
     const bf16_t* vbase = v + ((size_t)b * T * Hv + h) * D + j0;
@@ -393,123 +416,118 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
     const int rowk = Hk * D;             // element stride between tokens of q and k
     const int rowv = Hv * D;             // element stride between tokens of v and o
 
-    // state strip: tile a holds rows 16a + 4g + t, column jw + n
+    // State strip in accumulator layout.  Tile a, lane (g, n), element t holds
+    // state row lpos(16a + 4g + t) = 32(a >> 1) + 8g + 4(a & 1) + t, column jw + n:
+    // with rows in this order a tile pair is the K S operand with k in natural order.
+    const bool compute = w < SWAVES;
     f32x4 S[8];
-    if (h0) {
+    if (h0 && compute) {
         const float* hp = h0 + state_base + jw + n;
 #pragma unroll
         for (int a = 0; a < 8; ++a)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) S[a][t] = hp[(16 * a + 4 * g + t) * D];
+            for (int t = 0; t < 4; ++t) S[a][t] = hp[(32 * (a >> 1) + 8 * g + 4 * (a & 1) + t) * D];
     } else {
 #pragma unroll
         for (int a = 0; a < 8; ++a) S[a] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- prefetch registers of one chunk (branch-free: rows past the end
-    //      read a clamped valid row and are zeroed when staged)
-    uint4 pk[4], pq[4], pkt0, pkt1, pkt2, pkt3, pv0, pv1, pt0, pt1, pp0, pp1, pg;
-    auto prefetch = [&](int chunk) __attribute__((always_inline)) {
+    // ---- issue the direct loads of one chunk into buf[slot].  Rows past the
+    //      end read a clamped valid row: their beta is zero and the
+    //      precomputed k^T, T, P are zero there, so they contribute nothing.
+    auto load_chunk = [&](int chunk, int slot) __attribute__((always_inline)) {
+        ScanBuf& B = buf[slot];
+        const int lw = w - SWAVES;       // loader wave index
         const int t0 = chunk * C;
         const int last = min(C, T - t0) - 1;
         const bf16_t* kc = kbase + (size_t)t0 * rowk;
         const bf16_t* qc = qbase + (size_t)t0 * rowk;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int seg = tid + NT * u;
-            const int off = min(seg >> 4, last) * rowk + (seg & 15) * 8;
-            pk[u] = *reinterpret_cast<const uint4*>(kc + off);
-            pq[u] = *reinterpret_cast<const uint4*>(qc + off);
-        }
         const bf16_t* vc = vbase + (size_t)t0 * rowv;
-        const int c8 = (tid & 7) * 8;
-        pv0 = *reinterpret_cast<const uint4*>(vc + min(tid >> 3, last) * rowv + c8);
-        pv1 = *reinterpret_cast<const uint4*>(vc + min((tid + NT) >> 3, last) * rowv + c8);
+        // k, q: 16 blocks of 4 rows each
+#pragma unroll
+        for (int u = 0; u < 16 / LWAVES; ++u) {
+            const int blk = lw + LWAVES * u;
+            const int r = 4 * blk + (lane >> 4);
+            const int off = min(r, last) * rowk + 8 * ((lane & 15) ^ (r & 15));
+            lds_load16(kc + off, &B.K[64 * blk]);
+            lds_load16(qc + off, &B.Q[64 * blk]);
+        }
+        // workspace images: contiguous copies
         const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;
-        pt0 = *reinterpret_cast<const uint4*>(rec + WS_T + 16 * tid);
-        pt1 = *reinterpret_cast<const uint4*>(rec + WS_T + 16 * (tid + NT));
-        pp0 = *reinterpret_cast<const uint4*>(rec + WS_P + 16 * tid);
-        pp1 = *reinterpret_cast<const uint4*>(rec + WS_P + 16 * (tid + NT));
-        pg = *reinterpret_cast<const uint4*>(rec + WS_G + 16 * min(tid, NGATE * C / 4 - 1));
-        const unsigned char* ktc = kt0 + (size_t)chunk * WS_KT + 16 * tid;
-        pkt0 = *reinterpret_cast<const uint4*>(ktc);
-        pkt1 = *reinterpret_cast<const uint4*>(ktc + 16 * NT);
-        pkt2 = *reinterpret_cast<const uint4*>(ktc + 32 * NT);
-        pkt3 = *reinterpret_cast<const uint4*>(ktc + 48 * NT);
+        const unsigned char* ktc = kt0 + (size_t)chunk * WS_KT;
+#pragma unroll
+        for (int u = 0; u < 16 / LWAVES; ++u) {
+            const int blk = lw + LWAVES * u;
+            lds_load16(ktc + 1024 * blk + 16 * lane, &B.Kt[64 * blk]);
+        }
+#pragma unroll
+        for (int u = 0; u < 8 / LWAVES; ++u) {
+            const int blk = lw + LWAVES * u;
+            lds_load16(rec + WS_T + 1024 * blk + 16 * lane, &B.T[64 * blk]);
+            lds_load16(rec + WS_P + 1024 * blk + 16 * lane, &B.P[64 * blk]);
+        }
+        // v: 4 blocks of 16 rows (4 chunks of 16 bytes per row)
+#pragma unroll
+        for (int u = 0; u < 4 / LWAVES; ++u) {
+            const int blk = lw + LWAVES * u;
+            const int s = 16 * blk + (lane >> 2);
+            lds_load16(vc + min(s, last) * rowv + 8 * ((lane & 3) ^ ((s >> 2) & 3)), &B.V[64 * blk]);
+        }
+        // gates: 1280 bytes = one full block and 16 lanes of a second
+        if (lw == 0) {
+            lds_load16(rec + WS_G + 16 * lane, &B.gate[0]);
+        } else if (lane < 16) {
+            lds_load16(rec + WS_G + 1024 + 16 * lane, &B.gate[256]);
+        }
     };
-    // the previous chunk's output, from LDS to HBM in 16-byte rows
+    // the previous chunk's output tile, from LDS to HBM in 16-byte row pieces
     auto store_out = [&](int chunk) __attribute__((always_inline)) {
         const int t0 = chunk * C;
         const int L = min(C, T - t0);
         bf16_t* oc = obase + (size_t)t0 * rowv;
+        const uint16_t (*Ot)[OS] = Os[chunk & 1];
+        constexpr int LNT = 64 * LWAVES;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int seg = tid + NT * u;
-            const int r = seg >> 3;
+        for (int u = 0; u < C * BVS / 8 / LNT; ++u) {
+            const int seg = (tid - 64 * SWAVES) + LNT * u;
+            const int r = seg / (BVS / 8);
+            const int c8 = (seg % (BVS / 8)) * 8;
             if (r < L)
-                *reinterpret_cast<uint4*>(oc + r * rowv + (seg & 7) * 8) =
-                    *reinterpret_cast<const uint4*>(&sm.Os[r][(seg & 7) * 8]);
+                *reinterpret_cast<uint4*>(oc + r * rowv + c8) = *reinterpret_cast<const uint4*>(&Ot[r][c8]);
         }
     };
 
-    prefetch(0);
+    if (!compute) load_chunk(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
     for (int chunk = 0; chunk < NTc; ++chunk) {
-        const int L = min(C, T - chunk * C);
-        __syncthreads();  // (A) previous chunk's readers of LDS are done
-
-        // ---- stage: k, q rows with operand-order columns (8-byte groups); the rest as is
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int seg = tid + NT * u;
-            const int r = seg >> 4;
-            const int Q0 = (seg & 15) * 2;   // physical 4-groups Q0, Q0 + 1
-            const uint4 kv = mask4(pk[u], r < L);
-            const uint4 qv = mask4(pq[u], r < L);
-            const int c0 = 32 * (Q0 >> 3) + kperm(Q0 & 7);
-            const int c1 = 32 * ((Q0 + 1) >> 3) + kperm((Q0 + 1) & 7);
-            *reinterpret_cast<uint2*>(&sm.Kp[r][c0]) = make_uint2(kv.x, kv.y);
-            *reinterpret_cast<uint2*>(&sm.Kp[r][c1]) = make_uint2(kv.z, kv.w);
-            *reinterpret_cast<uint2*>(&sm.Qp[r][c0]) = make_uint2(qv.x, qv.y);
-            *reinterpret_cast<uint2*>(&sm.Qp[r][c1]) = make_uint2(qv.z, qv.w);
+        const int par = chunk & 1;
+        const ScanBuf& B = buf[par];
+        if (!compute) {
+            if (chunk > 0) store_out(chunk - 1);
+            if (chunk + 1 < NTc) load_chunk(chunk + 1, par ^ 1);
+            __builtin_amdgcn_s_waitcnt(0);   // the next chunk is in LDS
+            __syncthreads();
+            continue;
         }
-        {   // K^T: segment e holds row e >> 3, logical s (e & 7) * 8 .. + 7
-            const int c8 = (tid & 7) * 8, r0 = tid >> 3;
-            *reinterpret_cast<uint4*>(&sm.Ktp[r0][c8]) = pkt0;
-            *reinterpret_cast<uint4*>(&sm.Ktp[r0 + 32][c8]) = pkt1;
-            *reinterpret_cast<uint4*>(&sm.Ktp[r0 + 64][c8]) = pkt2;
-            *reinterpret_cast<uint4*>(&sm.Ktp[r0 + 96][c8]) = pkt3;
-        }
-        {
-            const int r0 = tid >> 3, r1 = (tid + NT) >> 3, c8 = (tid & 7) * 8;
-            *reinterpret_cast<uint4*>(&sm.Vr[r0][c8]) = mask4(pv0, r0 < L);
-            *reinterpret_cast<uint4*>(&sm.Vr[r1][c8]) = mask4(pv1, r1 < L);
-            *reinterpret_cast<uint4*>(&sm.Tp[r0][c8]) = pt0;
-            *reinterpret_cast<uint4*>(&sm.Tp[r1][c8]) = pt1;
-            *reinterpret_cast<uint4*>(&sm.Pp[r0][c8]) = pp0;
-            *reinterpret_cast<uint4*>(&sm.Pp[r1][c8]) = pp1;
-        }
-        if (tid < NGATE * C / 4) *reinterpret_cast<uint4*>(&sm.gate[0][0] + 4 * tid) = pg;
-        __syncthreads();  // (B)
-
-        // previous output out first, then the next chunk's loads
-        if (chunk > 0) store_out(chunk - 1);
-        if (chunk + 1 < NTc) prefetch(chunk + 1);
 
         // Operands are read from LDS in batches ahead of the MFMAs that use
-        // them (sched_barrier keeps the order): with one wave per SIMD nothing
-        // else would hide the LDS latency.
+        // them (sched_barrier keeps the order).
         // ---- gate vectors, v values and the K / Q operands of the first k step
         f32x4 btv[4], grk[4], grq[4];
         uint32_t vv[4][4];
+        const unsigned char* Vb = reinterpret_cast<const unsigned char*>(B.V);
+        const int vc = 2 * w + (n >> 3);          // 16-byte chunk of this lane's column
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int s0 = 16 * i + 4 * g;
-            btv[i] = *reinterpret_cast<const f32x4*>(&sm.gate[3][s0]);
-            grk[i] = *reinterpret_cast<const f32x4*>(&sm.gate[0][s0]);
-            grq[i] = *reinterpret_cast<const f32x4*>(&sm.gate[2][s0]);
+            btv[i] = *reinterpret_cast<const f32x4*>(&B.gate[3 * C + s0]);
+            grk[i] = *reinterpret_cast<const f32x4*>(&B.gate[0 * C + s0]);
+            grq[i] = *reinterpret_cast<const f32x4*>(&B.gate[2 * C + s0]);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) vv[i][t] = sm.Vr[s0 + t][jw - j0 + n];
+            for (int t = 0; t < 4; ++t)
+                vv[i][t] = *reinterpret_cast<const uint16_t*>(Vb + (s0 + t) * 64 + 16 * (vc ^ g) + 2 * (n & 7));
         }
         bf16x8 SB[4];
 #pragma unroll
@@ -523,8 +541,8 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
         bf16x8 ak[4], aq[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            ak[i] = ld8(&sm.Kp[16 * i + n][8 * g]);
-            aq[i] = ld8(&sm.Qp[16 * i + n][8 * g]);
+            ak[i] = __builtin_bit_cast(bf16x8, B.K[(16 * i + n) * 16 + (g ^ n)]);
+            aq[i] = __builtin_bit_cast(bf16x8, B.Q[(16 * i + n) * 16 + (g ^ n)]);
         }
         // ---- K S and Q S: k step outer, 8 independent accumulators inner
 #pragma unroll
@@ -533,8 +551,8 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
             if (ks < 3) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    nk[i] = ld8(&sm.Kp[16 * i + n][32 * (ks + 1) + 8 * g]);
-                    nq[i] = ld8(&sm.Qp[16 * i + n][32 * (ks + 1) + 8 * g]);
+                    nk[i] = __builtin_bit_cast(bf16x8, B.K[(16 * i + n) * 16 + ((4 * (ks + 1) + g) ^ n)]);
+                    nq[i] = __builtin_bit_cast(bf16x8, B.Q[(16 * i + n) * 16 + ((4 * (ks + 1) + g) ^ n)]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -553,11 +571,12 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
             }
         }
         // ---- T operands (needed next), issued before the X arithmetic
+        const int sw = n >> 1;                      // image swizzle of rows 16i + n
         bf16x8 at0[4], at1[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) at0[i] = ld8(&sm.Tp[16 * i + n][8 * g]);
-        at1[0] = ld8(&sm.Tp[32 + n][32 + 8 * g]);
-        at1[1] = ld8(&sm.Tp[48 + n][32 + 8 * g]);
+        for (int i = 0; i < 4; ++i) at0[i] = __builtin_bit_cast(bf16x8, B.T[(16 * i + n) * 8 + (g ^ sw)]);
+        at1[0] = __builtin_bit_cast(bf16x8, B.T[(32 + n) * 8 + ((4 + g) ^ sw)]);
+        at1[1] = __builtin_bit_cast(bf16x8, B.T[(48 + n) * 8 + ((4 + g) ^ sw)]);
         __builtin_amdgcn_sched_barrier(0);
         // ---- X = beta (V - Gamma rk K S)
         f32x4 X[4];
@@ -572,18 +591,18 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
         bf16x8 akt[8][2], ap0[4], ap1[2];
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
-            akt[a][0] = ld8(&sm.Ktp[16 * a + n][8 * g]);
-            akt[a][1] = ld8(&sm.Ktp[16 * a + n][32 + 8 * g]);
+            akt[a][0] = __builtin_bit_cast(bf16x8, B.Kt[(16 * a + n) * 8 + (g ^ sw)]);
+            akt[a][1] = __builtin_bit_cast(bf16x8, B.Kt[(16 * a + n) * 8 + ((4 + g) ^ sw)]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ap0[i] = ld8(&sm.Pp[16 * i + n][8 * g]);
-        ap1[0] = ld8(&sm.Pp[32 + n][32 + 8 * g]);
-        ap1[1] = ld8(&sm.Pp[48 + n][32 + 8 * g]);
-        const f32x4 wlo0 = *reinterpret_cast<const f32x4*>(&sm.gate[1][4 * g]);
-        const f32x4 whi0 = *reinterpret_cast<const f32x4*>(&sm.gate[1][16 + 4 * g]);
-        const f32x4 wlo1 = *reinterpret_cast<const f32x4*>(&sm.gate[1][32 + 4 * g]);
-        const f32x4 whi1 = *reinterpret_cast<const f32x4*>(&sm.gate[1][48 + 4 * g]);
-        const float GC = sm.gate[4][0];
+        for (int i = 0; i < 4; ++i) ap0[i] = __builtin_bit_cast(bf16x8, B.P[(16 * i + n) * 8 + (g ^ sw)]);
+        ap1[0] = __builtin_bit_cast(bf16x8, B.P[(32 + n) * 8 + ((4 + g) ^ sw)]);
+        ap1[1] = __builtin_bit_cast(bf16x8, B.P[(48 + n) * 8 + ((4 + g) ^ sw)]);
+        const f32x4 wlo0 = *reinterpret_cast<const f32x4*>(&B.gate[C + 4 * g]);
+        const f32x4 whi0 = *reinterpret_cast<const f32x4*>(&B.gate[C + 16 + 4 * g]);
+        const f32x4 wlo1 = *reinterpret_cast<const f32x4*>(&B.gate[C + 32 + 4 * g]);
+        const f32x4 whi1 = *reinterpret_cast<const f32x4*>(&B.gate[C + 48 + 4 * g]);
+        const float GC = B.gate[4 * C];
         __builtin_amdgcn_sched_barrier(0);
         // ---- Delta = T X (T lower triangular: row tile i needs k steps <= i/2)
         f32x4 Dl[4];
@@ -601,7 +620,7 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
         for (int a = 0; a < 8; ++a) S[a] = mfma32(akt[a][0], DWB0, S[a] * GC);
 #pragma unroll
         for (int a = 0; a < 8; ++a) S[a] = mfma32(akt[a][1], DWB1, S[a]);
-        // ---- output O = Gamma rq Q S + P Delta, into LDS (stored next chunk)
+        // ---- output O = Gamma rq Q S + P Delta, staged in LDS (stored next chunk)
         f32x4 O4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) O4[i] = mfma32(ap0[i], DB0, grq[i] * QS[i]);
@@ -611,17 +630,20 @@ __global__ __launch_bounds__(NT) void chunk_scan_kernel(
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                sm.Os[16 * i + 4 * g + t][SW * w + n] = static_cast<uint16_t>(bfbits(q_scale * O4[i][t]));
+                Os[par][16 * i + 4 * g + t][SW * w + n] = static_cast<uint16_t>(bfbits(q_scale * O4[i][t]));
+        __syncthreads();   // the loaders' next chunk is in LDS; this output is staged
     }
-    __syncthreads();
-    store_out(NTc - 1);
+    if (!compute) {
+        store_out(NTc - 1);
+        return;
+    }
 
     if (hT) {
         float* hp = hT + state_base + jw + n;
 #pragma unroll
         for (int a = 0; a < 8; ++a)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) hp[(16 * a + 4 * g + t) * D] = S[a][t];
+            for (int t = 0; t < 4; ++t) hp[(32 * (a >> 1) + 8 * g + 4 * (a & 1) + t) * D] = S[a][t];
     }
 }
 
@@ -650,7 +672,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
     if (err != hipSuccess) return err;
     const int scan_blocks = a.B * a.Hv * (D / BVS);
     const int remap = (scan_blocks % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(chunk_scan_kernel, dim3(scan_blocks), dim3(NT), 0, stream,
+    hipLaunchKernelGGL(chunk_scan_kernel, dim3(scan_blocks), dim3(SNT), 0, stream,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
                        static_cast<const bf16_t*>(a.v), ws, ws_kt, a.h0, a.hT,
                        static_cast<bf16_t*>(a.o), a.T, NTc, a.Hk, a.Hv, a.q_scale, remap);
