@@ -390,7 +390,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     __shared__ uint16_t Os[2][C][OS];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int g = lane >> 4;
     const int n = lane & 15;
 
@@ -497,20 +497,29 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
         }
     };
 
-    if (!compute) load_chunk(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
+    // The loader waves and the compute waves run separate loops that meet at
+    // one barrier per chunk (the wave index is uniform, so each wave takes one
+    // branch); keeping them apart keeps the loaders' address registers out of
+    // the compute waves' register budget.
+    if (!compute) {
+        load_chunk(0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int chunk = 0; chunk < NTc; ++chunk) {
+            const int par = chunk & 1;
+            if (chunk > 0) store_out(chunk - 1);
+            if (chunk + 1 < NTc) load_chunk(chunk + 1, par ^ 1);
+            __builtin_amdgcn_s_waitcnt(0);   // the next chunk is in LDS
+            __syncthreads();                 // ... and the compute waves staged this chunk's output
+        }
+        store_out(NTc - 1);
+        return;
+    }
     __syncthreads();
 
     for (int chunk = 0; chunk < NTc; ++chunk) {
         const int par = chunk & 1;
         const ScanBuf& B = buf[par];
-        if (!compute) {
-            if (chunk > 0) store_out(chunk - 1);
-            if (chunk + 1 < NTc) load_chunk(chunk + 1, par ^ 1);
-            __builtin_amdgcn_s_waitcnt(0);   // the next chunk is in LDS
-            __syncthreads();
-            continue;
-        }
 
         // Operands are read from LDS in batches ahead of the MFMAs that use
         // them (sched_barrier keeps the order).
@@ -632,10 +641,6 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
             for (int t = 0; t < 4; ++t)
                 Os[par][16 * i + 4 * g + t][SW * w + n] = static_cast<uint16_t>(bfbits(q_scale * O4[i][t]));
         __syncthreads();   // the loaders' next chunk is in LDS; this output is staged
-    }
-    if (!compute) {
-        store_out(NTc - 1);
-        return;
     }
 
     if (hT) {
