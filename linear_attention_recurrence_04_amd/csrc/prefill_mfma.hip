@@ -21,19 +21,22 @@
 //
 // Two kernels:
 //  * chunk_prep_kernel -- everything that does not depend on the state, for
-//    all chunks and heads at once (one workgroup per (b, value head, chunk)):
-//    row norms, the two Gram products (MFMA), gates, A, the triangular inverse
-//    T, and P.  T, P and the gate vectors go to the caller's workspace, T and P
-//    already in MFMA operand order.
+//    all chunks and heads at once (one workgroup per (b, key head, chunk)):
+//    row norms, k^T and the two Gram products (MFMA) once per key head; gates,
+//    A, the triangular inverse T and P for each value head of the group.  T, P
+//    and the gate vectors go to the caller's workspace, T and P already in
+//    MFMA operand order.
 //  * chunk_scan_kernel -- the serial chain over chunks.  One workgroup per
-//    (b, value head, 64 state columns); each wave owns a 16-column strip of
-//    the fp32 state for all 128 rows, in MFMA accumulator layout, for the whole
-//    sequence.  Per chunk a wave computes K S and Q S, X, Delta = T X, the
-//    output and the state update in its own registers: a pair of accumulator
-//    tiles is, element for element, a valid operand of the next product once
-//    the contraction index of the other operand is stored in the matching
-//    order (kperm below), so the chain needs no barrier and no LDS round trip.
-//    Chunk inputs are staged in LDS once per workgroup.
+//    (b, value head, 32 state columns).  Each of its two compute waves owns a
+//    16-column strip of the fp32 state for all 128 rows, in MFMA accumulator
+//    layout, for the whole sequence.  Per chunk a compute wave computes K S
+//    and Q S, X, Delta = T X, the output and the state update in its own
+//    registers: a pair of accumulator tiles is, element for element, a valid
+//    operand of the next product once the contraction index of the other
+//    operand is stored in the matching order (kperm below), so the chain needs
+//    no LDS round trip.  Two loader waves stream the next chunk's inputs into
+//    the other half of a double-buffered LDS area with direct global -> LDS
+//    loads and write the previous chunk's output.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -122,19 +125,32 @@ __host__ __device__ constexpr int img64(int r, int L) {
 __device__ __forceinline__ int ksb(int blk) { return 32 * (blk >> 2) + 4 * (blk & 3); }
 
 // ===========================================================================
-// prep: one workgroup per (b, value head h, chunk)
+// prep: one workgroup per (b, key head, chunk).  k, q, their norms, k^T and
+// the two Gram products are formed once for the Hv / Hk value heads that share
+// the key head; the gates, A, T and P once per value head.
 // ===========================================================================
 
+constexpr int GH = 4;   // value heads whose gates are prepared together (one per wave)
+
+// k and q rows are needed only up to the Gram products; the triangular
+// factors reuse their space (which keeps four workgroups on a CU).
 struct PrepSmem {
-    uint16_t Kr[C][SK];       // raw k rows (bf16)
-    uint16_t Qr[C][SK];       // raw q rows
-    uint16_t Ab[C][SC];       // A (bf16), physical order, off-diagonal blocks
-    uint16_t Tl[C][SC];       // T (bf16), physical order
-    float Af[4][16][17];      // A diagonal blocks (fp32)
-    float rk[C], rq[C], bt[C], gam[C];
+    union {
+        struct {
+            uint16_t Kr[C][SK];       // raw k rows (bf16)
+            uint16_t Qr[C][SK];       // raw q rows
+        } in;
+        struct {
+            uint16_t Ab[C][SC];       // A (bf16), physical order, off-diagonal blocks
+            uint16_t Tl[C][SC];       // T (bf16), physical order
+            float AfT[4][16][16];     // A diagonal blocks (fp32), transposed: [block][s][r]
+        } tri;
+    };
+    float rk[C], rq[C];
+    float gam[GH][C], bt[GH][C];
 };
 
-__global__ __launch_bounds__(NT) void chunk_prep_kernel(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const float* __restrict__ log_g, const float* __restrict__ beta,
     unsigned char* __restrict__ ws, unsigned char* __restrict__ ws_kt,
@@ -142,187 +158,65 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
     __shared__ PrepSmem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int g = lane >> 4;
     const int n = lane & 15;
 
     const int chunk = blockIdx.x % NTc;
-    const int bh = blockIdx.x / NTc;
-    const int b = bh / Hv;
-    const int h = bh - b * Hv;
-    const int hk = h / (Hv / Hk);
+    const int bk = blockIdx.x / NTc;
+    const int b = bk / Hk;
+    const int hk = bk - b * Hk;
+    const int rr = Hv / Hk;
     const int t0 = chunk * C;
     const int L = min(C, T - t0);
-    unsigned char* rec = ws + (size_t)blockIdx.x * WS_REC;
 
-    // ---- stage raw q, k rows (rows >= L are zero); zero the upper blocks of T
+    // gate inputs of value head hk * rr + jg + w for t0 + lane (clamped row;
+    // padding rows get g = 1, beta = 0 below), fetched one group ahead
+    auto gate_in = [&](int jg, float& lgr, float& btr) __attribute__((always_inline)) {
+        const int j = min(jg + w, rr - 1);
+        const size_t gi = ((size_t)b * T + t0 + min(lane, L - 1)) * Hv + hk * rr + j;
+        lgr = log_g[gi];
+        btr = beta[gi];
+    };
+    float lg_next, bt_next;
+    gate_in(0, lg_next, bt_next);
+
+    // ---- stage raw q, k rows (rows >= L are zero) and their inverse norms
+    //      (16 lanes per row)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int seg = tid + NT * u;
         const int r = seg >> 4;
         const int c8 = (seg & 15) * 8;
         const size_t off = (((size_t)b * T + t0 + min(r, L - 1)) * Hk + hk) * D + c8;
-        const uint4 kv = *reinterpret_cast<const uint4*>(k + off);
-        const uint4 qv = *reinterpret_cast<const uint4*>(q + off);
-        *reinterpret_cast<uint4*>(&sm.Kr[r][c8]) = mask4(kv, r < L);
-        *reinterpret_cast<uint4*>(&sm.Qr[r][c8]) = mask4(qv, r < L);
-    }
-    for (int e = tid; e < C * C; e += NT) {
-        const int r = e >> 6, s = e & 63;
-        if ((s >> 4) > (r >> 4)) sm.Tl[r][s] = 0;
-    }
-    float lg = 0.f, btv = 0.f;
-    if (w == 0) {   // padding rows: g = 1, beta = 0
-        const size_t gi = ((size_t)b * T + t0 + min(lane, L - 1)) * Hv + h;
-        const float lgr = log_g[gi], btr = beta[gi];
-        lg = (lane < L) ? lgr : 0.f;
-        btv = (lane < L) ? btr : 0.f;
-    }
-    __syncthreads();
-
-    // ---- row norms (4 threads per row); in-chunk decay scan (wave 0)
-    {
-        const int r = tid >> 2;
-        const int p = tid & 3;
+        const uint4 kv = mask4(*reinterpret_cast<const uint4*>(k + off), r < L);
+        const uint4 qv = mask4(*reinterpret_cast<const uint4*>(q + off), r < L);
+        *reinterpret_cast<uint4*>(&sm.in.Kr[r][c8]) = kv;
+        *reinterpret_cast<uint4*>(&sm.in.Qr[r][c8]) = qv;
+        const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
         float sk = 0.f, sq = 0.f;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const uint4 kk = *reinterpret_cast<const uint4*>(&sm.Kr[r][32 * p + 8 * x]);
-            const uint4 qq = *reinterpret_cast<const uint4*>(&sm.Qr[r][32 * p + 8 * x]);
-            const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
-            const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xffff0000u);
-                const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xffff0000u);
-                sk += k0 * k0 + k1 * k1;
-                sq += q0 * q0 + q1 * q1;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xffff0000u);
+            const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xffff0000u);
+            sk += k0 * k0 + k1 * k1;
+            sq += q0 * q0 + q1 * q1;
         }
-        sk = group_sum<4>(sk);
-        sq = group_sum<4>(sq);
-        if (p == 0) {
+        sk = group_sum<16>(sk);
+        sq = group_sum<16>(sq);
+        if ((lane & 15) == 0) {
             sm.rk[r] = l2norm ? inv_l2(sk) : 1.f;
             sm.rq[r] = l2norm ? inv_l2(sq) : 1.f;
         }
     }
-    float gam_l = 0.f;
-    if (w == 0) {
-        float x = lg;
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-            const float y = __shfl_up(x, m, 64);
-            if (lane >= m) x += y;
-        }
-        gam_l = x;
-        sm.gam[lane] = x;
-        sm.bt[lane] = btv;
-    }
     __syncthreads();
 
-    // ---- gates (wave 0): Gamma rk, exp(gamma_C - gamma) rk, Gamma rq, beta, Gamma_C
-    if (w == 0) {
-        const float total = __shfl(gam_l, 63, 64);
-        const float Gm = exp_hw(gam_l);
-        const float rkv = sm.rk[lane];
-        float* gp = reinterpret_cast<float*>(rec + WS_G);
-        gp[0 * C + lane] = Gm * rkv;
-        gp[1 * C + lane] = exp_hw(total - gam_l) * rkv;
-        gp[2 * C + lane] = Gm * sm.rq[lane];
-        gp[3 * C + lane] = btv;
-        gp[4 * C + lane] = exp_hw(total);
-    }
-
-    // ---- Gram tiles, computed transposed (s on the M side): 10 of K K^T -> A,
-    //      10 of Q K^T -> P.  Lane (g, n) ends with s = 16bb + 4g + t, r = 16a + n.
-    uint16_t* Pg = reinterpret_cast<uint16_t*>(rec + WS_P);
-#pragma unroll 1
-    for (int task = w; task < 20; task += 4) {
-        const bool is_qk = task >= 10;
-        int a, bb;
-        tile_of(is_qk ? task - 10 : task, a, bb);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* rowsB = is_qk ? &sm.Qr[16 * a + n][0] : &sm.Kr[16 * a + n][0];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            acc = mfma32(ld8(&sm.Kr[16 * bb + n][32 * ks + 8 * g]), ld8(rowsB + 32 * ks + 8 * g), acc);
-        const int r = 16 * a + n;
-        const float gr = sm.gam[r];
-        const float sr = is_qk ? sm.rq[r] : sm.rk[r] * sm.bt[r];
-        f32x4 val;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int s = 16 * bb + 4 * g + t;
-            const bool keep = is_qk ? (s <= r) : (s < r);
-            val[t] = keep ? exp_hw(gr - sm.gam[s]) * sr * sm.rk[s] * acc[t] : 0.f;
-        }
-        const int q4 = 4 * bb + g;   // physical 4-group of s
-        if (is_qk) {
-            *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (q4 >> 3) + kperm(q4 & 7))) = pack4(val);
-            if (a == bb && (a == 0 || a == 2)) {  // upper neighbour read by the scan: zero
-                const int qz = q4 + 4;
-                const s16x4 z = {0, 0, 0, 0};
-                *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (qz >> 3) + kperm(qz & 7))) = z;
-            }
-        } else if (a == bb) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) sm.Af[a][n][4 * g + t] = val[t];
-        } else {
-            *reinterpret_cast<s16x4*>(&sm.Ab[r][16 * bb + 4 * g]) = pack4(val);
-        }
-    }
-    __syncthreads();
-
-    // ---- diagonal blocks: T_ww = (I + A_ww)^-1 by forward substitution (lane = column)
-    if (lane < 16) {
-        float tc[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == n) ? 1.f : 0.f;
-#pragma unroll
-            for (int s = 0; s < r; ++s) acc -= sm.Af[w][r][s] * tc[s];
-            tc[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sm.Tl[16 * w + r][16 * w + n] = static_cast<uint16_t>(bfbits(tc[r]));
-    }
-    __syncthreads();
-
-    // ---- off-diagonal blocks of column block j = w:
-    //      (I + A_ii) T_ij + sum_{k=j}^{i-1} A_ik T_kj = 0  =>  T_ij = -T_ii sum_k A_ik T_kj
+    // ---- K^T for the key head: image row rho holds k column i = lpos(rho)
+    //      (the scan stores state rows in that order), s in operand order,
+    //      chunks swizzled as in img64
     {
-        const int j = w;
-        s16x4 tk[4];   // T_kj as operand (accumulator layout), k = j..3
-        {
-            s16x4 d;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) d[t] = static_cast<short>(sm.Tl[16 * j + 4 * g + t][16 * j + n]);
-            tk[0] = d;
-        }
-#pragma unroll
-        for (int di = 1; di < 4; ++di) {
-            const int i = j + di;
-            if (i < 4) {
-                f32x4 R = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int dk = 0; dk < di; ++dk)
-                    R = mfma16(ld4(&sm.Ab[16 * i + n][16 * (j + dk) + 4 * g]), tk[dk], R);
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 Tij = mfma16(ld4(&sm.Tl[16 * i + n][16 * i + 4 * g]), pack4(-R), zero);
-                tk[di] = pack4(Tij);
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    sm.Tl[16 * i + 4 * g + t][16 * j + n] = static_cast<uint16_t>(tk[di][t]);
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- K^T once per key head and chunk: image row rho holds k column
-    //      i = lpos(rho) (the scan stores state rows in that order), s in
-    //      operand order, chunks swizzled as in img64
-    if (h % (Hv / Hk) == 0) {
-        uint16_t* Kt = reinterpret_cast<uint16_t*>(ws_kt + (((size_t)b * Hk + hk) * NTc + chunk) * WS_KT);
+        uint16_t* Kt = reinterpret_cast<uint16_t*>(ws_kt + ((size_t)bk * NTc + chunk) * WS_KT);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int task = tid + NT * u;
@@ -334,21 +228,181 @@ __global__ __launch_bounds__(NT) void chunk_prep_kernel(
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int s0 = sb + 16 * (x >> 1) + 2 * (x & 1);
-                wd[x] = static_cast<uint32_t>(sm.Kr[s0][i]) | (static_cast<uint32_t>(sm.Kr[s0 + 1][i]) << 16);
+                wd[x] = static_cast<uint32_t>(sm.in.Kr[s0][i]) | (static_cast<uint32_t>(sm.in.Kr[s0 + 1][i]) << 16);
             }
             *reinterpret_cast<uint4*>(Kt + img64(rho, 8 * blk)) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
         }
     }
 
-    // ---- T to the workspace in operand order (8-byte groups, permuted per 32)
-    uint16_t* Tg = reinterpret_cast<uint16_t*>(rec + WS_T);
+    // ---- raw Gram tiles, computed transposed (s on the M side), kept in
+    //      registers: 10 of K K^T, 10 of Q K^T; wave w owns tasks w + 4u.
+    //      Lane (g, n) holds s = 16bb + 4g + t, r = 16a + n.
+    f32x4 gram[5];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int e = tid + NT * u;        // 1024 groups: row r, physical group Qg (16 per row)
-        const int r = e >> 4;
-        const int Qg = e & 15;
-        *reinterpret_cast<uint2*>(Tg + img64(r, 32 * (Qg >> 3) + kperm(Qg & 7))) =
-            *reinterpret_cast<const uint2*>(&sm.Tl[r][4 * Qg]);
+    for (int u = 0; u < 5; ++u) {
+        const int task = w + 4 * u;
+        const bool is_qk = task >= 10;
+        int a, bb;
+        tile_of(is_qk ? task - 10 : task, a, bb);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const uint16_t* rowsB = is_qk ? &sm.in.Qr[16 * a + n][0] : &sm.in.Kr[16 * a + n][0];
+        bf16x8 opa[4], opb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            opa[ks] = ld8(&sm.in.Kr[16 * bb + n][32 * ks + 8 * g]);
+            opb[ks] = ld8(rowsB + 32 * ks + 8 * g);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma32(opa[ks], opb[ks], acc);
+        gram[u] = acc;
+    }
+
+    for (int jg = 0; jg < rr; jg += GH) {
+        // ---- gates of value heads jg .. jg + GH - 1 (wave w: head jg + w):
+        //      decay scan, then Gamma rk, exp(gamma_C - gamma) rk, Gamma rq,
+        //      beta, Gamma_C to the record.  Padding rows: g = 1, beta = 0.
+        const float lgr = lg_next, btr = bt_next;
+        if (jg + GH < rr) gate_in(jg + GH, lg_next, bt_next);
+        if (jg + w < rr) {
+            const int h = hk * rr + jg + w;
+            float x = (lane < L) ? lgr : 0.f;
+            const float btv = (lane < L) ? btr : 0.f;
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) {
+                const float y = __shfl_up(x, m, 64);
+                if (lane >= m) x += y;
+            }
+            sm.gam[w][lane] = x;
+            sm.bt[w][lane] = btv;
+            const float total = __shfl(x, 63, 64);
+            const float Gm = exp_hw(x);
+            const float rkv = sm.rk[lane];
+            float* gp = reinterpret_cast<float*>(ws + (((size_t)b * Hv + h) * NTc + chunk) * WS_REC + WS_G);
+            gp[0 * C + lane] = Gm * rkv;
+            gp[1 * C + lane] = exp_hw(total - x) * rkv;
+            gp[2 * C + lane] = Gm * sm.rq[lane];
+            gp[3 * C + lane] = btv;
+            gp[4 * C + lane] = exp_hw(total);
+        }
+        __syncthreads();   // k and q rows are dead from here: their space holds A and T
+        if (jg == 0) {
+            for (int e = tid; e < C * C; e += NT) {   // upper blocks of T (never rewritten)
+                const int r = e >> 6, s2 = e & 63;
+                if ((s2 >> 4) > (r >> 4)) sm.tri.Tl[r][s2] = 0;
+            }
+        }
+
+        for (int jj = 0; jj < GH && jg + jj < rr; ++jj) {
+            const int h = hk * rr + jg + jj;
+            unsigned char* rec = ws + (((size_t)b * Hv + h) * NTc + chunk) * WS_REC;
+            const float* gam = sm.gam[jj];
+            const float* bt = sm.bt[jj];
+
+            // ---- gate the Gram tiles: A (diagonal blocks fp32 to LDS,
+            //      others bf16 to LDS), P straight to the record
+            uint16_t* Pg = reinterpret_cast<uint16_t*>(rec + WS_P);
+#pragma unroll
+            for (int u = 0; u < 5; ++u) {
+                const int task = w + 4 * u;
+                const bool is_qk = task >= 10;
+                int a, bb;
+                tile_of(is_qk ? task - 10 : task, a, bb);
+                const int r = 16 * a + n;
+                const float gr = gam[r];
+                const float sr = is_qk ? sm.rq[r] : sm.rk[r] * bt[r];
+                const f32x4 gs = *reinterpret_cast<const f32x4*>(&gam[16 * bb + 4 * g]);
+                const f32x4 ks = *reinterpret_cast<const f32x4*>(&sm.rk[16 * bb + 4 * g]);
+                f32x4 val;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int s2 = 16 * bb + 4 * g + t;
+                    const bool keep = is_qk ? (s2 <= r) : (s2 < r);
+                    const float x = exp_hw(gr - gs[t]) * sr * ks[t] * gram[u][t];
+                    val[t] = keep ? x : 0.f;
+                }
+                const int q4 = 4 * bb + g;   // physical 4-group of s
+                if (is_qk) {
+                    *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (q4 >> 3) + kperm(q4 & 7))) = pack4(val);
+                    if (a == bb && (a == 0 || a == 2)) {  // upper neighbour read by the scan: zero
+                        const int qz = q4 + 4;
+                        const s16x4 z = {0, 0, 0, 0};
+                        *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (qz >> 3) + kperm(qz & 7))) = z;
+                    }
+                } else if (a == bb) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) sm.tri.AfT[a][4 * g + t][n] = val[t];
+                } else {
+                    *reinterpret_cast<s16x4*>(&sm.tri.Ab[r][16 * bb + 4 * g]) = pack4(val);
+                }
+            }
+            __syncthreads();
+
+            // ---- diagonal blocks: T_ww = (I + A_ww)^-1 by forward substitution,
+            //      lane = column; once row s of the column is final its
+            //      multiples are removed from the rows below it
+            if (lane < 16) {
+                float tc[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tc[r] = (r == n) ? 1.f : 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < 15; ++s2) {
+                    float col[16];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sm.tri.AfT[w][s2][4 * x]);
+                        col[4 * x] = c4[0]; col[4 * x + 1] = c4[1]; col[4 * x + 2] = c4[2]; col[4 * x + 3] = c4[3];
+                    }
+#pragma unroll
+                    for (int r = s2 + 1; r < 16; ++r) tc[r] -= col[r] * tc[s2];
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sm.tri.Tl[16 * w + r][16 * w + n] = static_cast<uint16_t>(bfbits(tc[r]));
+            }
+            __syncthreads();
+
+            // ---- off-diagonal blocks of column block j = w:
+            //      (I + A_ii) T_ij + sum_{k=j}^{i-1} A_ik T_kj = 0  =>  T_ij = -T_ii sum_k A_ik T_kj
+            {
+                const int j = w;
+                s16x4 tk[4];   // T_kj as operand (accumulator layout), k = j..3
+                {
+                    s16x4 d;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) d[t] = static_cast<short>(sm.tri.Tl[16 * j + 4 * g + t][16 * j + n]);
+                    tk[0] = d;
+                }
+#pragma unroll
+                for (int di = 1; di < 4; ++di) {
+                    const int i = j + di;
+                    if (i < 4) {
+                        f32x4 R = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int dk = 0; dk < di; ++dk)
+                            R = mfma16(ld4(&sm.tri.Ab[16 * i + n][16 * (j + dk) + 4 * g]), tk[dk], R);
+                        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                        const f32x4 Tij = mfma16(ld4(&sm.tri.Tl[16 * i + n][16 * i + 4 * g]), pack4(-R), zero);
+                        tk[di] = pack4(Tij);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            sm.tri.Tl[16 * i + 4 * g + t][16 * j + n] = static_cast<uint16_t>(tk[di][t]);
+                    }
+                }
+            }
+            __syncthreads();
+
+            // ---- T to the record in operand order (8-byte groups, permuted
+            //      per 32).  The next head rewrites A first and T only after
+            //      its next barrier, so no barrier is needed here.
+            uint16_t* Tg = reinterpret_cast<uint16_t*>(rec + WS_T);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = tid + NT * u;        // 1024 groups: row r, physical group Qg (16 per row)
+                const int r = e >> 4;
+                const int Qg = e & 15;
+                *reinterpret_cast<uint2*>(Tg + img64(r, 32 * (Qg >> 3) + kperm(Qg & 7))) =
+                    *reinterpret_cast<const uint2*>(&sm.tri.Tl[r][4 * Qg]);
+            }
+        }
     }
 }
 
@@ -666,7 +720,7 @@ size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv) {
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
     using namespace mfma_prefill;
     const int NTc = (a.T + C - 1) / C;
-    const int prep_blocks = a.B * a.Hv * NTc;
+    const int prep_blocks = a.B * a.Hk * NTc;
     if (prep_blocks == 0) return hipSuccess;
     unsigned char* ws = static_cast<unsigned char*>(a.ws);
     unsigned char* ws_kt = ws + (size_t)a.B * a.Hv * NTc * WS_REC;
