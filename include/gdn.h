@@ -88,9 +88,8 @@ typedef struct {
  * the error.  The caller allocates the workspace; its contents need no
  * initialisation and are meaningless after the call.  The bf16 MFMA path
  * ("mfma_bf16" below) needs 17664 bytes per (sequence, value head, chunk of
- * 64 tokens) -- the chunk's triangular inverse, masked Q K^T and gate vectors,
- * computed for all chunks in parallel before the serial pass -- plus 16384
- * bytes per (sequence, key head, chunk) for the chunk's k transposed.
+ * 64 tokens): the chunk's triangular inverse, masked Q K^T and gate vectors,
+ * computed for all chunks in parallel before the serial pass.
  */
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* problem);
 

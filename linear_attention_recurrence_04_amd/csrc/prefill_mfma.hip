@@ -22,21 +22,23 @@
 // Two kernels:
 //  * chunk_prep_kernel -- everything that does not depend on the state, for
 //    all chunks and heads at once (one workgroup per (b, key head, chunk)):
-//    row norms, k^T and the two Gram products (MFMA) once per key head; gates,
+//    row norms and the two Gram products (MFMA) once per key head; gates,
 //    A, the triangular inverse T and P for each value head of the group.  T, P
 //    and the gate vectors go to the caller's workspace, T and P already in
 //    MFMA operand order.
 //  * chunk_scan_kernel -- the serial chain over chunks.  One workgroup per
-//    (b, value head, 32 state columns).  Each of its two compute waves owns a
+//    (b, value head, 32 state columns).  Each of its two state waves owns a
 //    16-column strip of the fp32 state for all 128 rows, in MFMA accumulator
-//    layout, for the whole sequence.  Per chunk a compute wave computes K S
-//    and Q S, X, Delta = T X, the output and the state update in its own
-//    registers: a pair of accumulator tiles is, element for element, a valid
-//    operand of the next product once the contraction index of the other
-//    operand is stored in the matching order (kperm below), so the chain needs
-//    no LDS round trip.  Two loader waves stream the next chunk's inputs into
-//    the other half of a double-buffered LDS area with direct global -> LDS
-//    loads and write the previous chunk's output.
+//    layout, for the whole sequence, and per chunk computes K S, X,
+//    Delta = T X and the state update in its own registers: a pair of
+//    accumulator tiles is, element for element, a valid operand of the next
+//    product once the contraction index of the other operand is stored in the
+//    matching order (kperm below).  The k^T operands of the update are read
+//    from the k rows in LDS with transposed LDS loads.  Two output waves, one
+//    chunk behind, form Q S + P Delta from the bf16 state and Delta operands
+//    the state waves leave in LDS, so the chain from chunk to chunk carries
+//    only K S, Delta and the update.  Two loader waves stream the inputs into
+//    double-buffered LDS with direct global -> LDS loads and store the output.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -60,9 +62,6 @@ constexpr int WS_P = C * C * 2;
 constexpr int WS_G = 2 * C * C * 2;
 constexpr int NGATE = 5;
 constexpr int WS_REC = WS_G + NGATE * C * 4;   // 17664 bytes
-// After all records: K^T per (b, key head, chunk), [128][64] bf16 with s in
-// operand order (written by the first value head of each key head).
-constexpr int WS_KT = D * C * 2;               // 16384 bytes
 
 // Contraction-index order inside each 32-wide k step.  A pair of accumulator
 // tiles (rows 32ks.., 32ks+16..) gives lane (g, n) the rows {4g..4g+3} and
@@ -120,13 +119,9 @@ __host__ __device__ constexpr int img64(int r, int L) {
     return r * 64 + 8 * ((L >> 3) ^ ((r >> 1) & 7)) + (L & 7);
 }
 
-// Order of the contraction index for the transposed k: logical s = 8 blk + x
-// (x = 0..7) is physical s = ksb(blk) + 16 (x >> 2) + (x & 3).
-__device__ __forceinline__ int ksb(int blk) { return 32 * (blk >> 2) + 4 * (blk & 3); }
-
 // ===========================================================================
-// prep: one workgroup per (b, key head, chunk).  k, q, their norms, k^T and
-// the two Gram products are formed once for the Hv / Hk value heads that share
+// prep: one workgroup per (b, key head, chunk).  k, q, their norms and the
+// two Gram products are formed once for the Hv / Hk value heads that share
 // the key head; the gates, A, T and P once per value head.
 // ===========================================================================
 
@@ -153,8 +148,7 @@ struct PrepSmem {
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const float* __restrict__ log_g, const float* __restrict__ beta,
-    unsigned char* __restrict__ ws, unsigned char* __restrict__ ws_kt,
-    int T, int NTc, int Hk, int Hv, int l2norm) {
+    unsigned char* __restrict__ ws, int T, int NTc, int Hk, int Hv, int l2norm) {
     __shared__ PrepSmem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -211,28 +205,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ch
         }
     }
     __syncthreads();
-
-    // ---- K^T for the key head: image row rho holds k column i = lpos(rho)
-    //      (the scan stores state rows in that order), s in operand order,
-    //      chunks swizzled as in img64
-    {
-        uint16_t* Kt = reinterpret_cast<uint16_t*>(ws_kt + ((size_t)bk * NTc + chunk) * WS_KT);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int task = tid + NT * u;
-            const int rho = task & (D - 1);
-            const int blk = task >> 7;          // logical s = 8 blk .. 8 blk + 7
-            const int i = lpos(rho);
-            const int sb = ksb(blk);
-            uint32_t wd[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int s0 = sb + 16 * (x >> 1) + 2 * (x & 1);
-                wd[x] = static_cast<uint32_t>(sm.in.Kr[s0][i]) | (static_cast<uint32_t>(sm.in.Kr[s0 + 1][i]) << 16);
-            }
-            *reinterpret_cast<uint4*>(Kt + img64(rho, 8 * blk)) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-        }
-    }
 
     // ---- raw Gram tiles, computed transposed (s on the M side), kept in
     //      registers: 10 of K K^T, 10 of Q K^T; wave w owns tasks w + 4u.
@@ -407,27 +379,45 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ch
 }
 
 // ===========================================================================
-// scan: one workgroup per (b, value head h, 32 state columns): two compute
-// waves (one per 16 columns) and two loader waves that stream the next
-// chunk's inputs into the other LDS buffer and store the previous output
+// scan: one workgroup per (b, value head h, 32 state columns), in three roles:
+//  * two state waves (one per 16-column strip): K S, X, Delta = T X and the
+//    state update, the chain that carries the state from chunk to chunk;
+//  * two output waves (one per strip), one chunk behind: Q S and P Delta from
+//    the bf16 state and Delta operands the state waves leave in LDS;
+//  * two loader waves: direct global -> LDS loads of the next chunk's inputs
+//    into double-buffered LDS, and the output stores.
+// All six meet at one barrier per chunk.
 // ===========================================================================
 
-constexpr int SW = 16;            // state columns per compute wave
-constexpr int SWAVES = 2;         // compute waves per workgroup
-constexpr int LWAVES = 2;         // loader waves per workgroup (global -> LDS, output stores)
-constexpr int SNT = 64 * (SWAVES + LWAVES);  // threads per workgroup
-constexpr int BVS = SW * SWAVES;  // state columns per workgroup
+constexpr int SW = 16;            // state columns per strip
+constexpr int NSTRIP = 2;         // strips per workgroup
+constexpr int LWAVES = 2;         // loader waves
+constexpr int SNT = 64 * (2 * NSTRIP + LWAVES);   // threads per workgroup
+constexpr int BVS = SW * NSTRIP;  // state columns per workgroup
 constexpr int OS = BVS + 8;       // row stride (elements) of the output staging tile
 
-// One chunk's inputs, as they arrive by direct global -> LDS loads.
-struct ScanBuf {
-    uint4 K[C * 16];       // k rows: chunk c of row r at c ^ (r & 15)
-    uint4 Q[C * 16];       // q rows, same
-    uint4 Kt[D * 8];       // k transposed image (img64 order)
+// 16-byte chunk c of a 256-byte k or q row r is stored at c ^ swz(r).  Row
+// operand reads (16 rows, one chunk) and transposed reads (4 rows x 4 chunks
+// per 16 lanes) both hit 16 distinct chunk positions.
+__host__ __device__ constexpr int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+struct KSet {              // state-wave inputs of one chunk
+    uint4 K[C * 16];       // k rows, swizzled
     uint4 T[C * 8];        // T image
-    uint4 P[C * 8];        // P image
-    uint4 V[C * 4];        // v block rows: chunk c of row s at c ^ ((s >> 2) & 3)
+    uint4 V[C * 4];        // v rows of the 32 columns: chunk c of row s at c ^ ((s >> 2) & 3)
     float gate[NGATE * C]; // grk, wrk, grq, beta, Gamma_C
+};
+struct QSet {              // output-wave inputs of one chunk
+    uint4 Q[C * 16];       // q rows, swizzled
+    uint4 P[C * 8];        // P image
+    float gate[NGATE * C];
+};
+struct ScanSmem {
+    KSet ks[2];
+    QSet qs[2];
+    bf16x8 Sx[2][NSTRIP][4][64];   // bf16 state operands (per strip, k step, lane)
+    bf16x8 Dx[2][NSTRIP][2][64];   // Delta operands
+    uint16_t Os[2][C][OS];         // output tile, stored by the loaders
 };
 
 // direct 16-byte load of one lane into LDS at base + 16 * lane (base wave-uniform)
@@ -435,13 +425,18 @@ __device__ __forceinline__ void lds_load16(const void* g, void* lds_base) {
     __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
 }
 
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// transposed 4 x 16-bit read: within each 16 lanes, lane i receives element
+// i & 3 of the 8-byte pieces addressed by lanes (i >> 2) + 4j, j = 0..3
+__device__ __forceinline__ s16x4 ld_tr4(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
 __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const unsigned char* __restrict__ ws, const unsigned char* __restrict__ ws_kt,
-    const float* h0, float* hT, bf16_t* __restrict__ o,
+    const unsigned char* __restrict__ ws, const float* h0, float* hT, bf16_t* __restrict__ o,
     int T, int NTc, int Hk, int Hv, float q_scale, int xcd_remap) {
-    __shared__ ScanBuf buf[2];
-    __shared__ uint16_t Os[2][C][OS];
+    __shared__ ScanSmem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -456,13 +451,11 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     constexpr int NB = D / BVS;          // column blocks per head
     const int bh = lid / NB;
     const int j0 = (lid % NB) * BVS;
-    const int jw = j0 + SW * w;          // this wave's first state column
     const int b = bh / Hv;
     const int h = bh - b * Hv;
     const int hk = h / (Hv / Hk);
     const size_t state_base = (size_t)bh * D * D;
     const unsigned char* rec0 = ws + (size_t)bh * NTc * WS_REC;
-    const unsigned char* kt0 = ws_kt + ((size_t)b * Hk + hk) * NTc * WS_KT;
     const bf16_t* kbase = k + ((size_t)b * T * Hk + hk) * D;
     const bf16_t* qbase = q + ((size_t)b * T * Hk + hk) * D;
     const bf16_t* vbase = v + ((size_t)b * T * Hv + h) * D + j0;
@@ -470,239 +463,285 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     const int rowk = Hk * D;             // element stride between tokens of q and k
     const int rowv = Hv * D;             // element stride between tokens of v and o
 
-    // State strip in accumulator layout.  Tile a, lane (g, n), element t holds
-    // state row lpos(16a + 4g + t) = 32(a >> 1) + 8g + 4(a & 1) + t, column jw + n:
-    // with rows in this order a tile pair is the K S operand with k in natural order.
-    const bool compute = w < SWAVES;
-    f32x4 S[8];
-    if (h0 && compute) {
-        const float* hp = h0 + state_base + jw + n;
+    // ======================= loader waves =======================
+    // Rows past the end read a clamped valid row: their beta is zero and their
+    // rows of T and P are those of the identity and zero, so they add nothing.
+    if (w >= 2 * NSTRIP) {
+        const int lw = w - 2 * NSTRIP;
+        auto load_gates = [&](const unsigned char* rec, float* gate) __attribute__((always_inline)) {
+            // 1280 bytes: one full 1 KiB block and 16 lanes of a second
+            if (lw == 0) lds_load16(rec + WS_G + 16 * lane, gate);
+            else if (lane < 16) lds_load16(rec + WS_G + 1024 + 16 * lane, gate + 256);
+        };
+        auto load_k = [&](int chunk, int slot) __attribute__((always_inline)) {
+            KSet& B = sm.ks[slot];
+            const int t0 = chunk * C;
+            const int last = min(C, T - t0) - 1;
+            const bf16_t* kc = kbase + (size_t)t0 * rowk;
+            const bf16_t* vc = vbase + (size_t)t0 * rowv;
+            const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;
 #pragma unroll
-        for (int a = 0; a < 8; ++a)
+            for (int u = 0; u < 16 / LWAVES; ++u) {   // 16 blocks of 4 rows
+                const int blk = lw + LWAVES * u;
+                const int r = 4 * blk + (lane >> 4);
+                lds_load16(kc + min(r, last) * rowk + 8 * ((lane & 15) ^ swz(r)), &B.K[64 * blk]);
+            }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) S[a][t] = hp[(32 * (a >> 1) + 8 * g + 4 * (a & 1) + t) * D];
-    } else {
+            for (int u = 0; u < 8 / LWAVES; ++u) {
+                const int blk = lw + LWAVES * u;
+                lds_load16(rec + WS_T + 1024 * blk + 16 * lane, &B.T[64 * blk]);
+            }
 #pragma unroll
-        for (int a = 0; a < 8; ++a) S[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    // ---- issue the direct loads of one chunk into buf[slot].  Rows past the
-    //      end read a clamped valid row: their beta is zero and the
-    //      precomputed k^T, T, P are zero there, so they contribute nothing.
-    auto load_chunk = [&](int chunk, int slot) __attribute__((always_inline)) {
-        ScanBuf& B = buf[slot];
-        const int lw = w - SWAVES;       // loader wave index
-        const int t0 = chunk * C;
-        const int last = min(C, T - t0) - 1;
-        const bf16_t* kc = kbase + (size_t)t0 * rowk;
-        const bf16_t* qc = qbase + (size_t)t0 * rowk;
-        const bf16_t* vc = vbase + (size_t)t0 * rowv;
-        // k, q: 16 blocks of 4 rows each
+            for (int u = 0; u < 4 / LWAVES; ++u) {    // 4 blocks of 16 rows
+                const int blk = lw + LWAVES * u;
+                const int s = 16 * blk + (lane >> 2);
+                lds_load16(vc + min(s, last) * rowv + 8 * ((lane & 3) ^ ((s >> 2) & 3)), &B.V[64 * blk]);
+            }
+            load_gates(rec, B.gate);
+        };
+        auto load_q = [&](int chunk, int slot) __attribute__((always_inline)) {
+            QSet& B = sm.qs[slot];
+            const int t0 = chunk * C;
+            const int last = min(C, T - t0) - 1;
+            const bf16_t* qc = qbase + (size_t)t0 * rowk;
+            const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;
 #pragma unroll
-        for (int u = 0; u < 16 / LWAVES; ++u) {
-            const int blk = lw + LWAVES * u;
-            const int r = 4 * blk + (lane >> 4);
-            const int off = min(r, last) * rowk + 8 * ((lane & 15) ^ (r & 15));
-            lds_load16(kc + off, &B.K[64 * blk]);
-            lds_load16(qc + off, &B.Q[64 * blk]);
-        }
-        // workspace images: contiguous copies
-        const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;
-        const unsigned char* ktc = kt0 + (size_t)chunk * WS_KT;
+            for (int u = 0; u < 16 / LWAVES; ++u) {
+                const int blk = lw + LWAVES * u;
+                const int r = 4 * blk + (lane >> 4);
+                lds_load16(qc + min(r, last) * rowk + 8 * ((lane & 15) ^ swz(r)), &B.Q[64 * blk]);
+            }
 #pragma unroll
-        for (int u = 0; u < 16 / LWAVES; ++u) {
-            const int blk = lw + LWAVES * u;
-            lds_load16(ktc + 1024 * blk + 16 * lane, &B.Kt[64 * blk]);
-        }
+            for (int u = 0; u < 8 / LWAVES; ++u) {
+                const int blk = lw + LWAVES * u;
+                lds_load16(rec + WS_P + 1024 * blk + 16 * lane, &B.P[64 * blk]);
+            }
+            load_gates(rec, B.gate);
+        };
+        // a finished output tile, from LDS to HBM in 16-byte row pieces
+        auto store_out = [&](int chunk) __attribute__((always_inline)) {
+            const int t0 = chunk * C;
+            const int L = min(C, T - t0);
+            bf16_t* oc = obase + (size_t)t0 * rowv;
+            const uint16_t (*Ot)[OS] = sm.Os[chunk & 1];
+            constexpr int LNT = 64 * LWAVES;
 #pragma unroll
-        for (int u = 0; u < 8 / LWAVES; ++u) {
-            const int blk = lw + LWAVES * u;
-            lds_load16(rec + WS_T + 1024 * blk + 16 * lane, &B.T[64 * blk]);
-            lds_load16(rec + WS_P + 1024 * blk + 16 * lane, &B.P[64 * blk]);
-        }
-        // v: 4 blocks of 16 rows (4 chunks of 16 bytes per row)
-#pragma unroll
-        for (int u = 0; u < 4 / LWAVES; ++u) {
-            const int blk = lw + LWAVES * u;
-            const int s = 16 * blk + (lane >> 2);
-            lds_load16(vc + min(s, last) * rowv + 8 * ((lane & 3) ^ ((s >> 2) & 3)), &B.V[64 * blk]);
-        }
-        // gates: 1280 bytes = one full block and 16 lanes of a second
-        if (lw == 0) {
-            lds_load16(rec + WS_G + 16 * lane, &B.gate[0]);
-        } else if (lane < 16) {
-            lds_load16(rec + WS_G + 1024 + 16 * lane, &B.gate[256]);
-        }
-    };
-    // the previous chunk's output tile, from LDS to HBM in 16-byte row pieces
-    auto store_out = [&](int chunk) __attribute__((always_inline)) {
-        const int t0 = chunk * C;
-        const int L = min(C, T - t0);
-        bf16_t* oc = obase + (size_t)t0 * rowv;
-        const uint16_t (*Ot)[OS] = Os[chunk & 1];
-        constexpr int LNT = 64 * LWAVES;
-#pragma unroll
-        for (int u = 0; u < C * BVS / 8 / LNT; ++u) {
-            const int seg = (tid - 64 * SWAVES) + LNT * u;
-            const int r = seg / (BVS / 8);
-            const int c8 = (seg % (BVS / 8)) * 8;
-            if (r < L)
-                *reinterpret_cast<uint4*>(oc + r * rowv + c8) = *reinterpret_cast<const uint4*>(&Ot[r][c8]);
-        }
-    };
-
-    // The loader waves and the compute waves run separate loops that meet at
-    // one barrier per chunk (the wave index is uniform, so each wave takes one
-    // branch); keeping them apart keeps the loaders' address registers out of
-    // the compute waves' register budget.
-    if (!compute) {
-        load_chunk(0, 0);
+            for (int u = 0; u < C * BVS / 8 / LNT; ++u) {
+                const int seg = 64 * lw + lane + LNT * u;
+                const int r = seg / (BVS / 8);
+                const int c8 = (seg % (BVS / 8)) * 8;
+                if (r < L)
+                    *reinterpret_cast<uint4*>(oc + r * rowv + c8) = *reinterpret_cast<const uint4*>(&Ot[r][c8]);
+            }
+        };
+        // iteration c: the state waves work on chunk c, the output waves on
+        // chunk c - 1; load k-side inputs of chunk c + 1 and q-side inputs of
+        // chunk c, store the output of chunk c - 2
+        load_k(0, 0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        for (int chunk = 0; chunk < NTc; ++chunk) {
-            const int par = chunk & 1;
-            if (chunk > 0) store_out(chunk - 1);
-            if (chunk + 1 < NTc) load_chunk(chunk + 1, par ^ 1);
-            __builtin_amdgcn_s_waitcnt(0);   // the next chunk is in LDS
-            __syncthreads();                 // ... and the compute waves staged this chunk's output
+        for (int c = 0; c <= NTc; ++c) {
+            if (c >= 2) store_out(c - 2);
+            if (c + 1 < NTc) load_k(c + 1, (c + 1) & 1);
+            if (c < NTc) load_q(c, c & 1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
         }
         store_out(NTc - 1);
         return;
     }
     __syncthreads();
 
-    for (int chunk = 0; chunk < NTc; ++chunk) {
-        const int par = chunk & 1;
-        const ScanBuf& B = buf[par];
+    const int strip = (w < NSTRIP) ? w : w - NSTRIP;
+    const int jw = j0 + SW * strip;      // first state column of the strip
+    const int sn = swz(n);               // swizzle of rows 16i + n
+    const int sw = n >> 1;               // image swizzle of rows 16i + n
 
-        // Operands are read from LDS in batches ahead of the MFMAs that use
-        // them (sched_barrier keeps the order).
-        // ---- gate vectors, v values and the K / Q operands of the first k step
-        f32x4 btv[4], grk[4], grq[4];
-        uint32_t vv[4][4];
-        const unsigned char* Vb = reinterpret_cast<const unsigned char*>(B.V);
-        const int vc = 2 * w + (n >> 3);          // 16-byte chunk of this lane's column
+    // ======================= state waves =======================
+    if (w < NSTRIP) {
+        // State strip in accumulator layout.  Tile a, lane (g, n), element t holds
+        // state row lpos(16a + 4g + t) = 32(a >> 1) + 8g + 4(a & 1) + t, column jw + n:
+        // with rows in this order a tile pair is the K S operand with k in natural order.
+        f32x4 S[8];
+        if (h0) {
+            const float* hp = h0 + state_base + jw + n;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int s0 = 16 * i + 4 * g;
-            btv[i] = *reinterpret_cast<const f32x4*>(&B.gate[3 * C + s0]);
-            grk[i] = *reinterpret_cast<const f32x4*>(&B.gate[0 * C + s0]);
-            grq[i] = *reinterpret_cast<const f32x4*>(&B.gate[2 * C + s0]);
+            for (int a = 0; a < 8; ++a)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                vv[i][t] = *reinterpret_cast<const uint16_t*>(Vb + (s0 + t) * 64 + 16 * (vc ^ g) + 2 * (n & 7));
+                for (int t = 0; t < 4; ++t) S[a][t] = hp[(32 * (a >> 1) + 8 * g + 4 * (a & 1) + t) * D];
+        } else {
+#pragma unroll
+            for (int a = 0; a < 8; ++a) S[a] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        bf16x8 SB[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) SB[ks] = pack8(S[2 * ks], S[2 * ks + 1]);
-        f32x4 KS[4], QS[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            KS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            QS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        bf16x8 ak[4], aq[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ak[i] = __builtin_bit_cast(bf16x8, B.K[(16 * i + n) * 16 + (g ^ n)]);
-            aq[i] = __builtin_bit_cast(bf16x8, B.Q[(16 * i + n) * 16 + (g ^ n)]);
-        }
-        // ---- K S and Q S: k step outer, 8 independent accumulators inner
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 nk[4], nq[4];
-            if (ks < 3) {
+        for (int c = 0; c <= NTc; ++c) {
+            if (c < NTc) {
+                const KSet& B = sm.ks[c & 1];
+                // ---- gate vectors, v values, the K operands of the first k step
+                f32x4 btv[4], grk[4];
+                uint32_t vv[4][4];
+                const unsigned char* Vb = reinterpret_cast<const unsigned char*>(B.V);
+                const int vc = 2 * strip + (n >> 3);      // 16-byte chunk of this lane's column
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    nk[i] = __builtin_bit_cast(bf16x8, B.K[(16 * i + n) * 16 + ((4 * (ks + 1) + g) ^ n)]);
-                    nq[i] = __builtin_bit_cast(bf16x8, B.Q[(16 * i + n) * 16 + ((4 * (ks + 1) + g) ^ n)]);
+                    const int s0 = 16 * i + 4 * g;
+                    btv[i] = *reinterpret_cast<const f32x4*>(&B.gate[3 * C + s0]);
+                    grk[i] = *reinterpret_cast<const f32x4*>(&B.gate[0 * C + s0]);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        vv[i][t] = *reinterpret_cast<const uint16_t*>(Vb + (s0 + t) * 64 + 16 * (vc ^ g) + 2 * (n & 7));
                 }
-            }
-            __builtin_amdgcn_sched_barrier(0);
+                bf16x8 SB[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                KS[i] = mfma32(ak[i], SB[ks], KS[i]);
-                QS[i] = mfma32(aq[i], SB[ks], QS[i]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if (ks < 3) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    ak[i] = nk[i];
-                    aq[i] = nq[i];
+                for (int ks = 0; ks < 4; ++ks) {
+                    SB[ks] = pack8(S[2 * ks], S[2 * ks + 1]);
+                    sm.Sx[c & 1][strip][ks][lane] = SB[ks];   // for the output wave
                 }
+                f32x4 KS[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) KS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                bf16x8 ak[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ak[i] = __builtin_bit_cast(bf16x8, B.K[(16 * i + n) * 16 + (g ^ sn)]);
+                // ---- K S: k step outer, 4 independent accumulators inner
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    bf16x8 nk[4];
+                    if (ks < 3) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            nk[i] = __builtin_bit_cast(bf16x8, B.K[(16 * i + n) * 16 + ((4 * (ks + 1) + g) ^ sn)]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) KS[i] = mfma32(ak[i], SB[ks], KS[i]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (ks < 3) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ak[i] = nk[i];
+                    }
+                }
+                // ---- T operands (needed next), issued before the X arithmetic
+                bf16x8 at0[4], at1[2];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) at0[i] = __builtin_bit_cast(bf16x8, B.T[(16 * i + n) * 8 + (g ^ sw)]);
+                at1[0] = __builtin_bit_cast(bf16x8, B.T[(32 + n) * 8 + ((4 + g) ^ sw)]);
+                at1[1] = __builtin_bit_cast(bf16x8, B.T[(48 + n) * 8 + ((4 + g) ^ sw)]);
+                __builtin_amdgcn_sched_barrier(0);
+                // ---- X = beta (V - Gamma rk K S)
+                f32x4 X[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        X[i][t] = btv[i][t] * (__uint_as_float(vv[i][t] << 16) - grk[i][t] * KS[i][t]);
+                const bf16x8 XB0 = pack8(X[0], X[1]);
+                const bf16x8 XB1 = pack8(X[2], X[3]);
+                // ---- k^T operands of the state update, read transposed from the
+                //      k rows: tile a, k step kk; lane (g, n) gets k column
+                //      lpos(16a + n) at tokens 32kk + 4g + j and 32kk + 16 + 4g + j
+                const unsigned char* Kb = reinterpret_cast<const unsigned char*>(B.K);
+                bf16x8 akt[8][2];
+#pragma unroll
+                for (int a = 0; a < 8; ++a)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const int r0 = 32 * kk + 4 * g + (n >> 2);
+                        const int ch = 4 * (a >> 1) + (n & 3);
+                        const int sz = ((n >> 2) << 2) | g;     // swz(r0) = swz(r0 + 16)
+                        const s16x4 lo = ld_tr4(Kb + r0 * 256 + 16 * (ch ^ sz) + 8 * (a & 1));
+                        const s16x4 hi = ld_tr4(Kb + (r0 + 16) * 256 + 16 * (ch ^ sz) + 8 * (a & 1));
+                        akt[a][kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
+                const f32x4 wlo0 = *reinterpret_cast<const f32x4*>(&B.gate[C + 4 * g]);
+                const f32x4 whi0 = *reinterpret_cast<const f32x4*>(&B.gate[C + 16 + 4 * g]);
+                const f32x4 wlo1 = *reinterpret_cast<const f32x4*>(&B.gate[C + 32 + 4 * g]);
+                const f32x4 whi1 = *reinterpret_cast<const f32x4*>(&B.gate[C + 48 + 4 * g]);
+                const float GC = B.gate[4 * C];
+                __builtin_amdgcn_sched_barrier(0);
+                // ---- Delta = T X (T lower triangular: row tile i needs k steps <= i/2)
+                f32x4 Dl[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Dl[i] = mfma32(at0[i], XB0, f32x4{0.f, 0.f, 0.f, 0.f});
+                Dl[2] = mfma32(at1[0], XB1, Dl[2]);
+                Dl[3] = mfma32(at1[1], XB1, Dl[3]);
+                // ---- Delta operands: plain (to the output wave) and scaled (state update)
+                sm.Dx[c & 1][strip][0][lane] = pack8(Dl[0], Dl[1]);
+                sm.Dx[c & 1][strip][1][lane] = pack8(Dl[2], Dl[3]);
+                const bf16x8 DWB0 = pack8(Dl[0] * wlo0, Dl[1] * whi0);
+                const bf16x8 DWB1 = pack8(Dl[2] * wlo1, Dl[3] * whi1);
+                // ---- state update S <- Gamma_C S + K^T (wrk Delta), 8 independent tiles
+#pragma unroll
+                for (int a = 0; a < 8; ++a) S[a] = mfma32(akt[a][0], DWB0, S[a] * GC);
+#pragma unroll
+                for (int a = 0; a < 8; ++a) S[a] = mfma32(akt[a][1], DWB1, S[a]);
             }
+            __syncthreads();
         }
-        // ---- T operands (needed next), issued before the X arithmetic
-        const int sw = n >> 1;                      // image swizzle of rows 16i + n
-        bf16x8 at0[4], at1[2];
+        if (hT) {
+            float* hp = hT + state_base + jw + n;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) at0[i] = __builtin_bit_cast(bf16x8, B.T[(16 * i + n) * 8 + (g ^ sw)]);
-        at1[0] = __builtin_bit_cast(bf16x8, B.T[(32 + n) * 8 + ((4 + g) ^ sw)]);
-        at1[1] = __builtin_bit_cast(bf16x8, B.T[(48 + n) * 8 + ((4 + g) ^ sw)]);
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- X = beta (V - Gamma rk K S)
-        f32x4 X[4];
+            for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                X[i][t] = btv[i][t] * (__uint_as_float(vv[i][t] << 16) - grk[i][t] * KS[i][t]);
-        const bf16x8 XB0 = pack8(X[0], X[1]);
-        const bf16x8 XB1 = pack8(X[2], X[3]);
-        // ---- state-update and output operands, issued before Delta = T X
-        bf16x8 akt[8][2], ap0[4], ap1[2];
-#pragma unroll
-        for (int a = 0; a < 8; ++a) {
-            akt[a][0] = __builtin_bit_cast(bf16x8, B.Kt[(16 * a + n) * 8 + (g ^ sw)]);
-            akt[a][1] = __builtin_bit_cast(bf16x8, B.Kt[(16 * a + n) * 8 + ((4 + g) ^ sw)]);
+                for (int t = 0; t < 4; ++t) hp[(32 * (a >> 1) + 8 * g + 4 * (a & 1) + t) * D] = S[a][t];
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ap0[i] = __builtin_bit_cast(bf16x8, B.P[(16 * i + n) * 8 + (g ^ sw)]);
-        ap1[0] = __builtin_bit_cast(bf16x8, B.P[(32 + n) * 8 + ((4 + g) ^ sw)]);
-        ap1[1] = __builtin_bit_cast(bf16x8, B.P[(48 + n) * 8 + ((4 + g) ^ sw)]);
-        const f32x4 wlo0 = *reinterpret_cast<const f32x4*>(&B.gate[C + 4 * g]);
-        const f32x4 whi0 = *reinterpret_cast<const f32x4*>(&B.gate[C + 16 + 4 * g]);
-        const f32x4 wlo1 = *reinterpret_cast<const f32x4*>(&B.gate[C + 32 + 4 * g]);
-        const f32x4 whi1 = *reinterpret_cast<const f32x4*>(&B.gate[C + 48 + 4 * g]);
-        const float GC = B.gate[4 * C];
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- Delta = T X (T lower triangular: row tile i needs k steps <= i/2)
-        f32x4 Dl[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Dl[i] = mfma32(at0[i], XB0, f32x4{0.f, 0.f, 0.f, 0.f});
-        Dl[2] = mfma32(at1[0], XB1, Dl[2]);
-        Dl[3] = mfma32(at1[1], XB1, Dl[3]);
-        // ---- operands of Delta: plain (output) and scaled (state update)
-        const bf16x8 DB0 = pack8(Dl[0], Dl[1]);
-        const bf16x8 DB1 = pack8(Dl[2], Dl[3]);
-        const bf16x8 DWB0 = pack8(Dl[0] * wlo0, Dl[1] * whi0);
-        const bf16x8 DWB1 = pack8(Dl[2] * wlo1, Dl[3] * whi1);
-        // ---- state update S <- Gamma_C S + K^T (wrk Delta), 8 independent tiles
-#pragma unroll
-        for (int a = 0; a < 8; ++a) S[a] = mfma32(akt[a][0], DWB0, S[a] * GC);
-#pragma unroll
-        for (int a = 0; a < 8; ++a) S[a] = mfma32(akt[a][1], DWB1, S[a]);
-        // ---- output O = Gamma rq Q S + P Delta, staged in LDS (stored next chunk)
-        f32x4 O4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O4[i] = mfma32(ap0[i], DB0, grq[i] * QS[i]);
-        O4[2] = mfma32(ap1[0], DB1, O4[2]);
-        O4[3] = mfma32(ap1[1], DB1, O4[3]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                Os[par][16 * i + 4 * g + t][SW * w + n] = static_cast<uint16_t>(bfbits(q_scale * O4[i][t]));
-        __syncthreads();   // the loaders' next chunk is in LDS; this output is staged
+        return;
     }
 
-    if (hT) {
-        float* hp = hT + state_base + jw + n;
+    // ======================= output waves =======================
+    for (int c = 0; c <= NTc; ++c) {
+        if (c >= 1) {
+            const int cc = c - 1;
+            const QSet& B = sm.qs[cc & 1];
+            // ---- operands: state and Delta from the state wave, q rows, P, gates
+            bf16x8 SB[4], aq[4];
 #pragma unroll
-        for (int a = 0; a < 8; ++a)
+            for (int ks = 0; ks < 4; ++ks) SB[ks] = sm.Sx[cc & 1][strip][ks][lane];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) hp[(32 * (a >> 1) + 8 * g + 4 * (a & 1) + t) * D] = S[a][t];
+            for (int i = 0; i < 4; ++i) aq[i] = __builtin_bit_cast(bf16x8, B.Q[(16 * i + n) * 16 + (g ^ sn)]);
+            f32x4 QS[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) QS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // ---- Q S
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                bf16x8 nq[4];
+                if (ks < 3) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        nq[i] = __builtin_bit_cast(bf16x8, B.Q[(16 * i + n) * 16 + ((4 * (ks + 1) + g) ^ sn)]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) QS[i] = mfma32(aq[i], SB[ks], QS[i]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (ks < 3) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) aq[i] = nq[i];
+                }
+            }
+            bf16x8 ap0[4], ap1[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ap0[i] = __builtin_bit_cast(bf16x8, B.P[(16 * i + n) * 8 + (g ^ sw)]);
+            ap1[0] = __builtin_bit_cast(bf16x8, B.P[(32 + n) * 8 + ((4 + g) ^ sw)]);
+            ap1[1] = __builtin_bit_cast(bf16x8, B.P[(48 + n) * 8 + ((4 + g) ^ sw)]);
+            const bf16x8 DB0 = sm.Dx[cc & 1][strip][0][lane];
+            const bf16x8 DB1 = sm.Dx[cc & 1][strip][1][lane];
+            f32x4 grq[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) grq[i] = *reinterpret_cast<const f32x4*>(&B.gate[2 * C + 16 * i + 4 * g]);
+            // ---- O = Gamma rq Q S + P Delta, staged in LDS for the loaders
+            f32x4 O4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O4[i] = mfma32(ap0[i], DB0, grq[i] * QS[i]);
+            O4[2] = mfma32(ap1[0], DB1, O4[2]);
+            O4[3] = mfma32(ap1[1], DB1, O4[3]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    sm.Os[cc & 1][16 * i + 4 * g + t][SW * strip + n] = static_cast<uint16_t>(bfbits(q_scale * O4[i][t]));
+        }
+        __syncthreads();
     }
 }
 
@@ -714,7 +753,8 @@ bool prefill_mfma_supported(const PrefillArgs& a) {
 
 size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv) {
     const size_t NTc = (size_t)(T + mfma_prefill::C - 1) / mfma_prefill::C;
-    return (size_t)B * Hv * NTc * mfma_prefill::WS_REC + (size_t)B * Hk * NTc * mfma_prefill::WS_KT;
+    (void)Hk;
+    return (size_t)B * Hv * NTc * mfma_prefill::WS_REC;
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
@@ -723,17 +763,16 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
     const int prep_blocks = a.B * a.Hk * NTc;
     if (prep_blocks == 0) return hipSuccess;
     unsigned char* ws = static_cast<unsigned char*>(a.ws);
-    unsigned char* ws_kt = ws + (size_t)a.B * a.Hv * NTc * WS_REC;
     hipLaunchKernelGGL(chunk_prep_kernel, dim3(prep_blocks), dim3(NT), 0, stream,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k), a.log_g, a.beta,
-                       ws, ws_kt, a.T, NTc, a.Hk, a.Hv, a.l2norm);
+                       ws, a.T, NTc, a.Hk, a.Hv, a.l2norm);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int scan_blocks = a.B * a.Hv * (D / BVS);
     const int remap = (scan_blocks % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL(chunk_scan_kernel, dim3(scan_blocks), dim3(SNT), 0, stream,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
-                       static_cast<const bf16_t*>(a.v), ws, ws_kt, a.h0, a.hT,
+                       static_cast<const bf16_t*>(a.v), ws, a.h0, a.hT,
                        static_cast<bf16_t*>(a.o), a.T, NTc, a.Hk, a.Hv, a.q_scale, remap);
     return hipGetLastError();
 }
