@@ -37,8 +37,9 @@
 //    from the k rows in LDS with transposed LDS loads.  Two output waves, one
 //    chunk behind, form Q S + P Delta from the bf16 state and Delta operands
 //    the state waves leave in LDS, so the chain from chunk to chunk carries
-//    only K S, Delta and the update.  Two loader waves stream the inputs into
-//    double-buffered LDS with direct global -> LDS loads and store the output.
+//    only K S, Delta and the update; they also store the output.  Four loader
+//    waves stream the inputs into double-buffered LDS with direct
+//    global -> LDS loads.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -383,15 +384,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ch
 //  * two state waves (one per 16-column strip): K S, X, Delta = T X and the
 //    state update, the chain that carries the state from chunk to chunk;
 //  * two output waves (one per strip), one chunk behind: Q S and P Delta from
-//    the bf16 state and Delta operands the state waves leave in LDS;
-//  * two loader waves: direct global -> LDS loads of the next chunk's inputs
-//    into double-buffered LDS, and the output stores.
-// All six meet at one barrier per chunk.
+//    the bf16 state and Delta operands the state waves leave in LDS, and the
+//    output stores;
+//  * four loader waves: direct global -> LDS loads of the next chunk's inputs
+//    into double-buffered LDS, and cache-line touches of the chunk after.
+// All eight meet at one barrier per chunk.
 // ===========================================================================
 
 constexpr int SW = 16;            // state columns per strip
 constexpr int NSTRIP = 2;         // strips per workgroup
-constexpr int LWAVES = 2;         // loader waves
+constexpr int LWAVES = 4;         // loader waves
 constexpr int SNT = 64 * (2 * NSTRIP + LWAVES);   // threads per workgroup
 constexpr int BVS = SW * NSTRIP;  // state columns per workgroup
 constexpr int OS = BVS + 8;       // row stride (elements) of the output staging tile
@@ -417,13 +419,22 @@ struct ScanSmem {
     QSet qs[2];
     bf16x8 Sx[2][NSTRIP][4][64];   // bf16 state operands (per strip, k step, lane)
     bf16x8 Dx[2][NSTRIP][2][64];   // Delta operands
-    uint16_t Os[2][C][OS];         // output tile, stored by the loaders
+    uint16_t Os[2][C][OS];         // output tiles, transposed to rows for 16-byte stores
+    uint32_t sink[LWAVES][64];     // landing area of the cache-line touches
 };
 
 // direct 16-byte load of one lane into LDS at base + 16 * lane (base wave-uniform)
 __device__ __forceinline__ void lds_load16(const void* g, void* lds_base) {
     __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
 }
+// 4-byte direct load: used to touch cache lines ahead of their use
+__device__ __forceinline__ void lds_load4(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(g, lds_base, 4, 0, 0);
+}
+// s_waitcnt immediate that waits until at most n vector memory operations are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt fields at their maximum, i.e. not waited for)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // transposed 4 x 16-bit read: within each 16 lanes, lane i receives element
@@ -468,86 +479,111 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     // rows of T and P are those of the identity and zero, so they add nothing.
     if (w >= 2 * NSTRIP) {
         const int lw = w - 2 * NSTRIP;
+        // per-lane byte offsets inside a chunk (rows clamped to `last`), so
+        // that each k, q or v load is a uniform base plus a 32-bit lane offset
+        constexpr int NKB = 16 / LWAVES, NVB = 4 / LWAVES, NRB = 8 / LWAVES;
+        uint32_t offk[NKB], offv[NVB];
+        auto set_offsets = [&](int last) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < NKB; ++u) {            // k / q: 16 blocks of 4 rows
+                const int r = 4 * (lw + LWAVES * u) + (lane >> 4);
+                offk[u] = 2u * (uint32_t)(min(r, last) * rowk + 8 * ((lane & 15) ^ swz(r)));
+            }
+#pragma unroll
+            for (int u = 0; u < NVB; ++u) {            // v: 4 blocks of 16 rows
+                const int s2 = 16 * (lw + LWAVES * u) + (lane >> 2);
+                offv[u] = 2u * (uint32_t)(min(s2, last) * rowv + 8 * ((lane & 3) ^ ((s2 >> 2) & 3)));
+            }
+        };
+        set_offsets(C - 1);
         auto load_gates = [&](const unsigned char* rec, float* gate) __attribute__((always_inline)) {
             // 1280 bytes: one full 1 KiB block and 16 lanes of a second
             if (lw == 0) lds_load16(rec + WS_G + 16 * lane, gate);
-            else if (lane < 16) lds_load16(rec + WS_G + 1024 + 16 * lane, gate + 256);
+            else if (lw == 1 && lane < 16) lds_load16(rec + WS_G + 1024 + 16 * lane, gate + 256);
         };
         auto load_k = [&](int chunk, int slot) __attribute__((always_inline)) {
             KSet& B = sm.ks[slot];
             const int t0 = chunk * C;
-            const int last = min(C, T - t0) - 1;
-            const bf16_t* kc = kbase + (size_t)t0 * rowk;
-            const bf16_t* vc = vbase + (size_t)t0 * rowv;
+            const unsigned char* kc = reinterpret_cast<const unsigned char*>(kbase + (size_t)t0 * rowk);
+            const unsigned char* vc = reinterpret_cast<const unsigned char*>(vbase + (size_t)t0 * rowv);
             const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;
 #pragma unroll
-            for (int u = 0; u < 16 / LWAVES; ++u) {   // 16 blocks of 4 rows
-                const int blk = lw + LWAVES * u;
-                const int r = 4 * blk + (lane >> 4);
-                lds_load16(kc + min(r, last) * rowk + 8 * ((lane & 15) ^ swz(r)), &B.K[64 * blk]);
-            }
+            for (int u = 0; u < NKB; ++u) lds_load16(kc + offk[u], &B.K[64 * (lw + LWAVES * u)]);
 #pragma unroll
-            for (int u = 0; u < 8 / LWAVES; ++u) {
+            for (int u = 0; u < NRB; ++u) {
                 const int blk = lw + LWAVES * u;
                 lds_load16(rec + WS_T + 1024 * blk + 16 * lane, &B.T[64 * blk]);
             }
 #pragma unroll
-            for (int u = 0; u < 4 / LWAVES; ++u) {    // 4 blocks of 16 rows
-                const int blk = lw + LWAVES * u;
-                const int s = 16 * blk + (lane >> 2);
-                lds_load16(vc + min(s, last) * rowv + 8 * ((lane & 3) ^ ((s >> 2) & 3)), &B.V[64 * blk]);
-            }
+            for (int u = 0; u < NVB; ++u) lds_load16(vc + offv[u], &B.V[64 * (lw + LWAVES * u)]);
             load_gates(rec, B.gate);
         };
         auto load_q = [&](int chunk, int slot) __attribute__((always_inline)) {
             QSet& B = sm.qs[slot];
             const int t0 = chunk * C;
-            const int last = min(C, T - t0) - 1;
-            const bf16_t* qc = qbase + (size_t)t0 * rowk;
+            const unsigned char* qc = reinterpret_cast<const unsigned char*>(qbase + (size_t)t0 * rowk);
             const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;
 #pragma unroll
-            for (int u = 0; u < 16 / LWAVES; ++u) {
-                const int blk = lw + LWAVES * u;
-                const int r = 4 * blk + (lane >> 4);
-                lds_load16(qc + min(r, last) * rowk + 8 * ((lane & 15) ^ swz(r)), &B.Q[64 * blk]);
-            }
+            for (int u = 0; u < NKB; ++u) lds_load16(qc + offk[u], &B.Q[64 * (lw + LWAVES * u)]);
 #pragma unroll
-            for (int u = 0; u < 8 / LWAVES; ++u) {
+            for (int u = 0; u < NRB; ++u) {
                 const int blk = lw + LWAVES * u;
                 lds_load16(rec + WS_P + 1024 * blk + 16 * lane, &B.P[64 * blk]);
             }
             load_gates(rec, B.gate);
         };
-        // a finished output tile, from LDS to HBM in 16-byte row pieces
-        auto store_out = [&](int chunk) __attribute__((always_inline)) {
+        // one 4-byte load per 128-byte line of a chunk's inputs (two per
+        // loader wave), so that their direct loads a chunk later hit L2
+        constexpr int NTOUCH = 2;
+        auto touch = [&](int chunk) __attribute__((always_inline)) {
             const int t0 = chunk * C;
-            const int L = min(C, T - t0);
-            bf16_t* oc = obase + (size_t)t0 * rowv;
-            const uint16_t (*Ot)[OS] = sm.Os[chunk & 1];
-            constexpr int LNT = 64 * LWAVES;
-#pragma unroll
-            for (int u = 0; u < C * BVS / 8 / LNT; ++u) {
-                const int seg = 64 * lw + lane + LNT * u;
-                const int r = seg / (BVS / 8);
-                const int c8 = (seg % (BVS / 8)) * 8;
-                if (r < L)
-                    *reinterpret_cast<uint4*>(oc + r * rowv + c8) = *reinterpret_cast<const uint4*>(&Ot[r][c8]);
+            const int lane_row = t0 + min(lane, T - t0 - 1);
+            uint32_t* sink = sm.sink[lw];
+            const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;   // 138 lines
+            if (lw == 0) {
+                lds_load4(rec + 128 * lane, sink);
+                lds_load4(rec + 128 * (64 + lane), sink);
+            } else if (lw == 1) {
+                lds_load4(rec + 128 * min(128 + lane, WS_REC / 128 - 1), sink);
+                lds_load4(vbase + (size_t)lane_row * rowv, sink);
+            } else {
+                const bf16_t* base = (lw == 2) ? kbase : qbase;
+                lds_load4(base + (size_t)lane_row * rowk, sink);
+                lds_load4(base + (size_t)lane_row * rowk + 64, sink);
             }
         };
-        // iteration c: the state waves work on chunk c, the output waves on
-        // chunk c - 1; load k-side inputs of chunk c + 1 and q-side inputs of
-        // chunk c, store the output of chunk c - 2
+        static_assert(LWAVES == 4, "the touches are spread over four loader waves");
+        // iteration c: the state waves work on chunk c and the output waves on
+        // chunk c - 1; load the q-side inputs of chunk c and the k-side inputs
+        // of chunk c + 1, touch chunk c + 2.  Loads of the last chunk (k side
+        // first) come after every load of the earlier chunks, so the offsets
+        // switch to its clamped rows once.
+        if (NTc == 1) set_offsets(T - 1);
         load_k(0, 0);
+        if (NTc > 1) touch(1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int c = 0; c <= NTc; ++c) {
-            if (c >= 2) store_out(c - 2);
-            if (c + 1 < NTc) load_k(c + 1, (c + 1) & 1);
             if (c < NTc) load_q(c, c & 1);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+            if (c + 1 < NTc) {
+                if (c + 1 == NTc - 1) set_offsets(T - (NTc - 1) * C - 1);
+                load_k(c + 1, (c + 1) & 1);
+            }
+            if (c + 2 < NTc) {
+                // vector memory operations complete in issue order: waiting
+                // until only the touches are outstanding waits for the loads
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                touch(c + 2);
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(NTOUCH));
+            } else {
+                __builtin_amdgcn_s_waitcnt(0);
+            }
+            // the plain barrier: a fenced one would also wait for the touches
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
         }
-        store_out(NTc - 1);
         return;
     }
     __syncthreads();
@@ -729,17 +765,31 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
             f32x4 grq[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) grq[i] = *reinterpret_cast<const f32x4*>(&B.gate[2 * C + 16 * i + 4 * g]);
-            // ---- O = Gamma rq Q S + P Delta, staged in LDS for the loaders
+            // ---- O = Gamma rq Q S + P Delta
             f32x4 O4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) O4[i] = mfma32(ap0[i], DB0, grq[i] * QS[i]);
             O4[2] = mfma32(ap1[0], DB1, O4[2]);
             O4[3] = mfma32(ap1[1], DB1, O4[3]);
+            uint16_t (*Ot)[OS] = sm.Os[cc & 1];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    sm.Os[cc & 1][16 * i + 4 * g + t][SW * strip + n] = static_cast<uint16_t>(bfbits(q_scale * O4[i][t]));
+                    Ot[16 * i + 4 * g + t][SW * strip + n] = static_cast<uint16_t>(bfbits(q_scale * O4[i][t]));
+            // ---- the strip's 64 rows x 32 bytes back from LDS (this wave's own
+            //      writes, so no barrier) and to HBM in 16-byte pieces
+            const int t0 = cc * C;
+            const int L = min(C, T - t0);
+            bf16_t* oc = obase + (size_t)t0 * rowv + SW * strip;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r = (lane >> 1) + 32 * u;
+                const int c8 = 8 * (lane & 1);
+                if (r < L)
+                    *reinterpret_cast<uint4*>(oc + r * rowv + c8) =
+                        *reinterpret_cast<const uint4*>(&Ot[r][SW * strip + c8]);
+            }
         }
         __syncthreads();
     }
