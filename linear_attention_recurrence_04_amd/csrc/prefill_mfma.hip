@@ -387,7 +387,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ch
 //    the bf16 state and Delta operands the state waves leave in LDS, and the
 //    output stores;
 //  * four loader waves: direct global -> LDS loads of the next chunk's inputs
-//    into double-buffered LDS, and cache-line touches of the chunk after.
+//    into double-buffered LDS.
 // All eight meet at one barrier per chunk.
 // ===========================================================================
 
@@ -420,22 +420,12 @@ struct ScanSmem {
     bf16x8 Sx[2][NSTRIP][4][64];   // bf16 state operands (per strip, k step, lane)
     bf16x8 Dx[2][NSTRIP][2][64];   // Delta operands
     uint16_t Os[2][C][OS];         // output tiles, transposed to rows for 16-byte stores
-    uint32_t sink[LWAVES][64];     // landing area of the cache-line touches
 };
 
 // direct 16-byte load of one lane into LDS at base + 16 * lane (base wave-uniform)
 __device__ __forceinline__ void lds_load16(const void* g, void* lds_base) {
     __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
 }
-// 4-byte direct load: used to touch cache lines ahead of their use
-__device__ __forceinline__ void lds_load4(const void* g, void* lds_base) {
-    __builtin_amdgcn_global_load_lds(g, lds_base, 4, 0, 0);
-}
-// s_waitcnt immediate that waits until at most n vector memory operations are
-// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
-// lgkmcnt fields at their maximum, i.e. not waited for)
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // transposed 4 x 16-bit read: within each 16 lanes, lane i receives element
 // i & 3 of the 8-byte pieces addressed by lanes (i >> 2) + 4j, j = 0..3
@@ -532,35 +522,13 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
             }
             load_gates(rec, B.gate);
         };
-        // one 4-byte load per 128-byte line of a chunk's inputs (two per
-        // loader wave), so that their direct loads a chunk later hit L2
-        constexpr int NTOUCH = 2;
-        auto touch = [&](int chunk) __attribute__((always_inline)) {
-            const int t0 = chunk * C;
-            const int lane_row = t0 + min(lane, T - t0 - 1);
-            uint32_t* sink = sm.sink[lw];
-            const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;   // 138 lines
-            if (lw == 0) {
-                lds_load4(rec + 128 * lane, sink);
-                lds_load4(rec + 128 * (64 + lane), sink);
-            } else if (lw == 1) {
-                lds_load4(rec + 128 * min(128 + lane, WS_REC / 128 - 1), sink);
-                lds_load4(vbase + (size_t)lane_row * rowv, sink);
-            } else {
-                const bf16_t* base = (lw == 2) ? kbase : qbase;
-                lds_load4(base + (size_t)lane_row * rowk, sink);
-                lds_load4(base + (size_t)lane_row * rowk + 64, sink);
-            }
-        };
-        static_assert(LWAVES == 4, "the touches are spread over four loader waves");
         // iteration c: the state waves work on chunk c and the output waves on
         // chunk c - 1; load the q-side inputs of chunk c and the k-side inputs
-        // of chunk c + 1, touch chunk c + 2.  Loads of the last chunk (k side
-        // first) come after every load of the earlier chunks, so the offsets
-        // switch to its clamped rows once.
+        // of chunk c + 1.  Loads of the last chunk (k side first) come after
+        // every load of the earlier chunks, so the offsets switch to its
+        // clamped rows once.
         if (NTc == 1) set_offsets(T - 1);
         load_k(0, 0);
-        if (NTc > 1) touch(1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int c = 0; c <= NTc; ++c) {
@@ -569,20 +537,8 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 if (c + 1 == NTc - 1) set_offsets(T - (NTc - 1) * C - 1);
                 load_k(c + 1, (c + 1) & 1);
             }
-            if (c + 2 < NTc) {
-                // vector memory operations complete in issue order: waiting
-                // until only the touches are outstanding waits for the loads
-                asm volatile("" ::: "memory");
-                __builtin_amdgcn_sched_barrier(0);
-                touch(c + 2);
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(NTOUCH));
-            } else {
-                __builtin_amdgcn_s_waitcnt(0);
-            }
-            // the plain barrier: a fenced one would also wait for the touches
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0);   // this iteration's loads are in LDS
+            __syncthreads();
         }
         return;
     }

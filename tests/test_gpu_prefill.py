@@ -198,3 +198,14 @@ def test_mfma_edges(T):
     o, hT = run_prefill(inp, "bf16", 64)
     o_ref, h_ref = run_oracle(inp)
     assert_parity(host(o), o_ref, host(hT), h_ref, "bf16", f"mfma T={T}")
+
+
+@pytest.mark.parametrize("Hk,Hv", [(1, 4), (1, 5), (1, 8), (2, 16)])
+def test_mfma_gqa_ratios(Hk, Hv):
+    """Value heads per key head beyond one group of four (the prep kernel
+    prepares gates for four value heads at a time)."""
+    say(f"mfma gqa {Hk}x{Hv}")
+    inp = gi.custom_prefill(2, 130, Hk, Hv, 128, 128, seed=Hv, dtype="bf16", gate="qwen", h0="normal")
+    o, hT = run_prefill(inp, "bf16", 64)
+    o_ref, h_ref = run_oracle(inp)
+    assert_parity(host(o), o_ref, host(hT), h_ref, "bf16", f"mfma {Hk}x{Hv}")
