@@ -126,10 +126,16 @@ __host__ __device__ constexpr int img64(int r, int L) {
 // the key head; the gates, A, T and P once per value head.
 // ===========================================================================
 
-constexpr int GH = 4;   // value heads whose gates are prepared together (one per wave)
+constexpr int GH = 4;   // value heads prepared together (one per wave for the gates,
+                        // one per 16-lane group in the diagonal solve)
+
+// Lower-triangular 16x16 blocks of a 64x64 matrix, stored compactly:
+// diagonal and below (i >= j) at tl_idx, strictly below (i > k) at ab_idx.
+__host__ __device__ constexpr int tl_idx(int i, int j) { return i * (i + 1) / 2 + j; }
+__host__ __device__ constexpr int ab_idx(int i, int k) { return i * (i - 1) / 2 + k; }
 
 // k and q rows are needed only up to the Gram products; the triangular
-// factors reuse their space (which keeps four workgroups on a CU).
+// factors of the group's value heads reuse their space.
 struct PrepSmem {
     union {
         struct {
@@ -137,9 +143,9 @@ struct PrepSmem {
             uint16_t Qr[C][SK];       // raw q rows
         } in;
         struct {
-            uint16_t Ab[C][SC];       // A (bf16), physical order, off-diagonal blocks
-            uint16_t Tl[C][SC];       // T (bf16), physical order
-            float AfT[4][16][16];     // A diagonal blocks (fp32), transposed: [block][s][r]
+            float AfT[GH][4][16][16];      // A diagonal blocks (fp32), transposed: [head][block][s][r]
+            uint16_t Ab[GH][6][16][16];    // A blocks below the diagonal (bf16)
+            uint16_t Tl[GH][10][16][16];   // T blocks on and below the diagonal (bf16)
         } tri;
     };
     float rk[C], rq[C];
@@ -231,12 +237,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ch
     }
 
     for (int jg = 0; jg < rr; jg += GH) {
+        const int nh = min(GH, rr - jg);   // value heads in this group
         // ---- gates of value heads jg .. jg + GH - 1 (wave w: head jg + w):
         //      decay scan, then Gamma rk, exp(gamma_C - gamma) rk, Gamma rq,
         //      beta, Gamma_C to the record.  Padding rows: g = 1, beta = 0.
         const float lgr = lg_next, btr = bt_next;
         if (jg + GH < rr) gate_in(jg + GH, lg_next, bt_next);
-        if (jg + w < rr) {
+        if (w < nh) {
             const int h = hk * rr + jg + w;
             float x = (lane < L) ? lgr : 0.f;
             const float btv = (lane < L) ? btr : 0.f;
@@ -258,122 +265,130 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ch
             gp[4 * C + lane] = exp_hw(total);
         }
         __syncthreads();   // k and q rows are dead from here: their space holds A and T
-        if (jg == 0) {
-            for (int e = tid; e < C * C; e += NT) {   // upper blocks of T (never rewritten)
-                const int r = e >> 6, s2 = e & 63;
-                if ((s2 >> 4) > (r >> 4)) sm.tri.Tl[r][s2] = 0;
+
+        // ---- gate the Gram tiles for every head of the group: A (diagonal
+        //      blocks fp32, others bf16) to LDS, P straight to the record
+#pragma unroll
+        for (int u = 0; u < 5; ++u) {
+            const int task = w + 4 * u;
+            const bool is_qk = task >= 10;
+            int a, bb;
+            tile_of(is_qk ? task - 10 : task, a, bb);
+            const int r = 16 * a + n;
+            const f32x4 ks = *reinterpret_cast<const f32x4*>(&sm.rk[16 * bb + 4 * g]);
+            const float srr = is_qk ? sm.rq[r] : sm.rk[r];
+#pragma unroll
+            for (int hh = 0; hh < GH; ++hh) {
+                if (hh < nh) {
+                    const float* gam = sm.gam[hh];
+                    const float gr = gam[r];
+                    const float sr = is_qk ? srr : srr * sm.bt[hh][r];
+                    const f32x4 gs = *reinterpret_cast<const f32x4*>(&gam[16 * bb + 4 * g]);
+                    f32x4 val;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int s2 = 16 * bb + 4 * g + t;
+                        const bool keep = is_qk ? (s2 <= r) : (s2 < r);
+                        const float x = exp_hw(gr - gs[t]) * sr * ks[t] * gram[u][t];
+                        val[t] = keep ? x : 0.f;
+                    }
+                    if (is_qk) {
+                        const int h = hk * rr + jg + hh;
+                        uint16_t* Pg = reinterpret_cast<uint16_t*>(ws + (((size_t)b * Hv + h) * NTc + chunk) * WS_REC + WS_P);
+                        const int q4 = 4 * bb + g;   // physical 4-group of s
+                        *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (q4 >> 3) + kperm(q4 & 7))) = pack4(val);
+                        if (a == bb && (a == 0 || a == 2)) {  // upper neighbour read by the scan: zero
+                            const int qz = q4 + 4;
+                            const s16x4 z = {0, 0, 0, 0};
+                            *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (qz >> 3) + kperm(qz & 7))) = z;
+                        }
+                    } else if (a == bb) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) sm.tri.AfT[hh][a][4 * g + t][n] = val[t];
+                    } else {
+                        *reinterpret_cast<s16x4*>(&sm.tri.Ab[hh][ab_idx(a, bb)][n][4 * g]) = pack4(val);
+                    }
+                }
             }
         }
+        __syncthreads();
 
-        for (int jj = 0; jj < GH && jg + jj < rr; ++jj) {
-            const int h = hk * rr + jg + jj;
-            unsigned char* rec = ws + (((size_t)b * Hv + h) * NTc + chunk) * WS_REC;
-            const float* gam = sm.gam[jj];
-            const float* bt = sm.bt[jj];
-
-            // ---- gate the Gram tiles: A (diagonal blocks fp32 to LDS,
-            //      others bf16 to LDS), P straight to the record
-            uint16_t* Pg = reinterpret_cast<uint16_t*>(rec + WS_P);
+        // ---- diagonal blocks: T_ww = (I + A_ww)^-1 by forward substitution.
+        //      Wave w solves block w for every head at once: lane (g, n) is
+        //      column n of head g.  Once row s of the column is final, its
+        //      multiples are removed from the rows below it.
+        {
+            const int hh = g;
+            float tc[16];
 #pragma unroll
-            for (int u = 0; u < 5; ++u) {
-                const int task = w + 4 * u;
-                const bool is_qk = task >= 10;
-                int a, bb;
-                tile_of(is_qk ? task - 10 : task, a, bb);
-                const int r = 16 * a + n;
-                const float gr = gam[r];
-                const float sr = is_qk ? sm.rq[r] : sm.rk[r] * bt[r];
-                const f32x4 gs = *reinterpret_cast<const f32x4*>(&gam[16 * bb + 4 * g]);
-                const f32x4 ks = *reinterpret_cast<const f32x4*>(&sm.rk[16 * bb + 4 * g]);
-                f32x4 val;
+            for (int r = 0; r < 16; ++r) tc[r] = (r == n) ? 1.f : 0.f;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int s2 = 16 * bb + 4 * g + t;
-                    const bool keep = is_qk ? (s2 <= r) : (s2 < r);
-                    const float x = exp_hw(gr - gs[t]) * sr * ks[t] * gram[u][t];
-                    val[t] = keep ? x : 0.f;
+            for (int s2 = 0; s2 < 15; ++s2) {
+                float col[16];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sm.tri.AfT[hh][w][s2][4 * x]);
+                    col[4 * x] = c4[0]; col[4 * x + 1] = c4[1]; col[4 * x + 2] = c4[2]; col[4 * x + 3] = c4[3];
                 }
-                const int q4 = 4 * bb + g;   // physical 4-group of s
-                if (is_qk) {
-                    *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (q4 >> 3) + kperm(q4 & 7))) = pack4(val);
-                    if (a == bb && (a == 0 || a == 2)) {  // upper neighbour read by the scan: zero
-                        const int qz = q4 + 4;
-                        const s16x4 z = {0, 0, 0, 0};
-                        *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (qz >> 3) + kperm(qz & 7))) = z;
-                    }
-                } else if (a == bb) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) sm.tri.AfT[a][4 * g + t][n] = val[t];
-                } else {
-                    *reinterpret_cast<s16x4*>(&sm.tri.Ab[r][16 * bb + 4 * g]) = pack4(val);
-                }
+                for (int r = s2 + 1; r < 16; ++r) tc[r] -= col[r] * tc[s2];
             }
-            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.tri.Tl[hh][tl_idx(w, w)][r][n] = static_cast<uint16_t>(bfbits(tc[r]));
+        }
+        __syncthreads();
 
-            // ---- diagonal blocks: T_ww = (I + A_ww)^-1 by forward substitution,
-            //      lane = column; once row s of the column is final its
-            //      multiples are removed from the rows below it
-            if (lane < 16) {
-                float tc[16];
+        // ---- blocks below the diagonal in column block j = w, every head:
+        //      (I + A_ii) T_ij + sum_{k=j}^{i-1} A_ik T_kj = 0  =>  T_ij = -T_ii sum_k A_ik T_kj
+        {
+            const int j = w;
+            s16x4 tk[GH][4];   // T_kj as operand (accumulator layout), k = j..3
 #pragma unroll
-                for (int r = 0; r < 16; ++r) tc[r] = (r == n) ? 1.f : 0.f;
+            for (int hh = 0; hh < GH; ++hh) {
+                s16x4 d;
 #pragma unroll
-                for (int s2 = 0; s2 < 15; ++s2) {
-                    float col[16];
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sm.tri.AfT[w][s2][4 * x]);
-                        col[4 * x] = c4[0]; col[4 * x + 1] = c4[1]; col[4 * x + 2] = c4[2]; col[4 * x + 3] = c4[3];
-                    }
-#pragma unroll
-                    for (int r = s2 + 1; r < 16; ++r) tc[r] -= col[r] * tc[s2];
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sm.tri.Tl[16 * w + r][16 * w + n] = static_cast<uint16_t>(bfbits(tc[r]));
+                for (int t = 0; t < 4; ++t) d[t] = static_cast<short>(sm.tri.Tl[hh][tl_idx(j, j)][4 * g + t][n]);
+                tk[hh][0] = d;
             }
-            __syncthreads();
-
-            // ---- off-diagonal blocks of column block j = w:
-            //      (I + A_ii) T_ij + sum_{k=j}^{i-1} A_ik T_kj = 0  =>  T_ij = -T_ii sum_k A_ik T_kj
-            {
-                const int j = w;
-                s16x4 tk[4];   // T_kj as operand (accumulator layout), k = j..3
-                {
-                    s16x4 d;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) d[t] = static_cast<short>(sm.tri.Tl[16 * j + 4 * g + t][16 * j + n]);
-                    tk[0] = d;
-                }
+            for (int di = 1; di < 4; ++di) {
+                const int i = j + di;
+                if (i < 4) {
 #pragma unroll
-                for (int di = 1; di < 4; ++di) {
-                    const int i = j + di;
-                    if (i < 4) {
-                        f32x4 R = {0.f, 0.f, 0.f, 0.f};
+                    for (int hh = 0; hh < GH; ++hh) {
+                        if (hh < nh) {
+                            f32x4 R = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int dk = 0; dk < di; ++dk)
-                            R = mfma16(ld4(&sm.tri.Ab[16 * i + n][16 * (j + dk) + 4 * g]), tk[dk], R);
-                        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                        const f32x4 Tij = mfma16(ld4(&sm.tri.Tl[16 * i + n][16 * i + 4 * g]), pack4(-R), zero);
-                        tk[di] = pack4(Tij);
+                            for (int dk = 0; dk < di; ++dk)
+                                R = mfma16(ld4(&sm.tri.Ab[hh][ab_idx(i, j + dk)][n][4 * g]), tk[hh][dk], R);
+                            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                            const f32x4 Tij = mfma16(ld4(&sm.tri.Tl[hh][tl_idx(i, i)][n][4 * g]), pack4(-R), zero);
+                            tk[hh][di] = pack4(Tij);
 #pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            sm.tri.Tl[16 * i + 4 * g + t][16 * j + n] = static_cast<uint16_t>(tk[di][t]);
+                            for (int t = 0; t < 4; ++t)
+                                sm.tri.Tl[hh][tl_idx(i, j)][4 * g + t][n] = static_cast<uint16_t>(tk[hh][di][t]);
+                        }
                     }
                 }
             }
-            __syncthreads();
+        }
+        __syncthreads();
 
-            // ---- T to the record in operand order (8-byte groups, permuted
-            //      per 32).  The next head rewrites A first and T only after
-            //      its next barrier, so no barrier is needed here.
-            uint16_t* Tg = reinterpret_cast<uint16_t*>(rec + WS_T);
+        // ---- T of every head to its record in operand order (8-byte groups,
+        //      permuted per 32); blocks above the diagonal are zero.  The next
+        //      group rewrites A first and T only after its next barrier.
+        for (int hh = 0; hh < nh; ++hh) {
+            const int h = hk * rr + jg + hh;
+            uint16_t* Tg = reinterpret_cast<uint16_t*>(ws + (((size_t)b * Hv + h) * NTc + chunk) * WS_REC + WS_T);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int e = tid + NT * u;        // 1024 groups: row r, physical group Qg (16 per row)
                 const int r = e >> 4;
                 const int Qg = e & 15;
-                *reinterpret_cast<uint2*>(Tg + img64(r, 32 * (Qg >> 3) + kperm(Qg & 7))) =
-                    *reinterpret_cast<const uint2*>(&sm.tri.Tl[r][4 * Qg]);
+                const int bi = r >> 4, bj = Qg >> 2;
+                uint2 val = make_uint2(0u, 0u);
+                if (bj <= bi) val = *reinterpret_cast<const uint2*>(&sm.tri.Tl[hh][tl_idx(bi, bj)][r & 15][4 * (Qg & 3)]);
+                *reinterpret_cast<uint2*>(Tg + img64(r, 32 * (Qg >> 3) + kperm(Qg & 7))) = val;
             }
         }
     }
