@@ -111,6 +111,8 @@ __device__ __forceinline__ void tile_of(int idx, int& a, int& b) {
     a = (idx >= 1) + (idx >= 3) + (idx >= 6);
     b = idx - (a * (a + 1)) / 2;
 }
+__host__ __device__ constexpr int tile_a(int idx) { return (idx >= 1) + (idx >= 3) + (idx >= 6); }
+__host__ __device__ constexpr int tile_b(int idx) { return idx - (tile_a(idx) * (tile_a(idx) + 1)) / 2; }
 
 // The [rows][64] bf16 images (T, P, k transposed) are read by the scan as
 // 16-byte MFMA operands; chunk c (logical columns 8c..8c+7) of row r is stored
@@ -151,6 +153,68 @@ struct PrepSmem {
     float rk[C], rq[C];
     float gam[GH][C], bt[GH][C];
 };
+
+// Gating of one wave's five Gram tiles (tasks W, W + 4, .., W + 16: tasks
+// 0..9 are K K^T tiles, 10..19 Q K^T tiles) for the nh value heads of a
+// group, with the tile geometry known at compile time so that every LDS
+// read of a head is issued before its arithmetic.  Lane (g, n) holds
+// s = 16bb + 4g + t, r = 16a + n.  A goes to LDS (diagonal blocks fp32,
+// others bf16); P goes to the record of each head (rec0 + hh * rec_stride).
+template <int W>
+__device__ __forceinline__ void gate_tiles(PrepSmem& sm, const f32x4 (&gram)[5], int nh, int g, int n,
+                                           unsigned char* rec0, size_t rec_stride) {
+    f32x4 ks[4];
+    float rkr[4], rqr[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        ks[x] = *reinterpret_cast<const f32x4*>(&sm.rk[16 * x + 4 * g]);
+        rkr[x] = sm.rk[16 * x + n];
+        rqr[x] = sm.rq[16 * x + n];
+    }
+#pragma unroll 1
+    for (int hh = 0; hh < nh; ++hh) {
+        float gr[4], btr[4];
+        f32x4 gs[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            gr[x] = sm.gam[hh][16 * x + n];
+            btr[x] = sm.bt[hh][16 * x + n];
+            gs[x] = *reinterpret_cast<const f32x4*>(&sm.gam[hh][16 * x + 4 * g]);
+        }
+        uint16_t* Pg = reinterpret_cast<uint16_t*>(rec0 + hh * rec_stride + WS_P);
+#pragma unroll
+        for (int u = 0; u < 5; ++u) {
+            const int task = W + 4 * u;
+            const bool is_qk = task >= 10;
+            const int a = tile_a(is_qk ? task - 10 : task);
+            const int bb = tile_b(is_qk ? task - 10 : task);
+            const int r = 16 * a + n;
+            const float sr = is_qk ? rqr[a] : rkr[a] * btr[a];
+            f32x4 val;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int s2 = 16 * bb + 4 * g + t;
+                const bool keep = is_qk ? (s2 <= r) : (s2 < r);
+                const float x = exp_hw(gr[a] - gs[bb][t]) * sr * ks[bb][t] * gram[u][t];
+                val[t] = keep ? x : 0.f;
+            }
+            if (is_qk) {
+                const int q4 = 4 * bb + g;   // physical 4-group of s
+                *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (q4 >> 3) + kperm(q4 & 7))) = pack4(val);
+                if (a == bb && (a == 0 || a == 2)) {  // upper neighbour read by the scan: zero
+                    const int qz = q4 + 4;
+                    const s16x4 z = {0, 0, 0, 0};
+                    *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (qz >> 3) + kperm(qz & 7))) = z;
+                }
+            } else if (a == bb) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) sm.tri.AfT[hh][a][4 * g + t][n] = val[t];
+            } else {
+                *reinterpret_cast<s16x4*>(&sm.tri.Ab[hh][ab_idx(a, bb)][n][4 * g]) = pack4(val);
+            }
+        }
+    }
+}
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -268,47 +332,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ch
 
         // ---- gate the Gram tiles for every head of the group: A (diagonal
         //      blocks fp32, others bf16) to LDS, P straight to the record
-#pragma unroll
-        for (int u = 0; u < 5; ++u) {
-            const int task = w + 4 * u;
-            const bool is_qk = task >= 10;
-            int a, bb;
-            tile_of(is_qk ? task - 10 : task, a, bb);
-            const int r = 16 * a + n;
-            const f32x4 ks = *reinterpret_cast<const f32x4*>(&sm.rk[16 * bb + 4 * g]);
-            const float srr = is_qk ? sm.rq[r] : sm.rk[r];
-#pragma unroll
-            for (int hh = 0; hh < GH; ++hh) {
-                if (hh < nh) {
-                    const float* gam = sm.gam[hh];
-                    const float gr = gam[r];
-                    const float sr = is_qk ? srr : srr * sm.bt[hh][r];
-                    const f32x4 gs = *reinterpret_cast<const f32x4*>(&gam[16 * bb + 4 * g]);
-                    f32x4 val;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int s2 = 16 * bb + 4 * g + t;
-                        const bool keep = is_qk ? (s2 <= r) : (s2 < r);
-                        const float x = exp_hw(gr - gs[t]) * sr * ks[t] * gram[u][t];
-                        val[t] = keep ? x : 0.f;
-                    }
-                    if (is_qk) {
-                        const int h = hk * rr + jg + hh;
-                        uint16_t* Pg = reinterpret_cast<uint16_t*>(ws + (((size_t)b * Hv + h) * NTc + chunk) * WS_REC + WS_P);
-                        const int q4 = 4 * bb + g;   // physical 4-group of s
-                        *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (q4 >> 3) + kperm(q4 & 7))) = pack4(val);
-                        if (a == bb && (a == 0 || a == 2)) {  // upper neighbour read by the scan: zero
-                            const int qz = q4 + 4;
-                            const s16x4 z = {0, 0, 0, 0};
-                            *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (qz >> 3) + kperm(qz & 7))) = z;
-                        }
-                    } else if (a == bb) {
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) sm.tri.AfT[hh][a][4 * g + t][n] = val[t];
-                    } else {
-                        *reinterpret_cast<s16x4*>(&sm.tri.Ab[hh][ab_idx(a, bb)][n][4 * g]) = pack4(val);
-                    }
-                }
+        {
+            unsigned char* rec0 = ws + (((size_t)b * Hv + hk * rr + jg) * NTc + chunk) * WS_REC;
+            const size_t rec_stride = (size_t)NTc * WS_REC;
+            switch (w) {
+                case 0: gate_tiles<0>(sm, gram, nh, g, n, rec0, rec_stride); break;
+                case 1: gate_tiles<1>(sm, gram, nh, g, n, rec0, rec_stride); break;
+                case 2: gate_tiles<2>(sm, gram, nh, g, n, rec0, rec_stride); break;
+                default: gate_tiles<3>(sm, gram, nh, g, n, rec0, rec_stride); break;
             }
         }
         __syncthreads();
