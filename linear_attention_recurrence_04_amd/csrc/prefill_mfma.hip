@@ -49,6 +49,7 @@ namespace mfma_prefill {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 constexpr int D = 128;      // head dim (dk = dv)
 constexpr int C = 64;       // chunk
@@ -102,6 +103,20 @@ __device__ __forceinline__ s16x4 ld4(const uint16_t* p) { return *reinterpret_ca
 __device__ __forceinline__ uint4 mask4(uint4 x, bool keep) {
     const uint32_t m = keep ? 0xffffffffu : 0u;
     return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+}
+// Sum over each row of 16 lanes with DPP moves: swap neighbours, swap pairs,
+// mirror within 8 lanes, mirror within 16 lanes.  Every lane of the row ends
+// with the row's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_mov<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += dpp_mov<0x141>(x);   // row_half_mirror
+    x += dpp_mov<0x140>(x);   // row_mirror
+    return x;
 }
 // exp(x) through the hardware base-2 exponential (arguments here are <= 0)
 __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
@@ -247,29 +262,34 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ch
     gate_in(0, lg_next, bt_next);
 
     // ---- stage raw q, k rows (rows >= L are zero) and their inverse norms
-    //      (16 lanes per row)
+    //      (16 lanes per row); all eight loads are issued first
+    u32x4 kv[4], qv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int seg = tid + NT * u;
-        const int r = seg >> 4;
-        const int c8 = (seg & 15) * 8;
+        const int r = (tid + NT * u) >> 4;
+        const int c8 = (tid & 15) * 8;
         const size_t off = (((size_t)b * T + t0 + min(r, L - 1)) * Hk + hk) * D + c8;
-        const uint4 kv = mask4(*reinterpret_cast<const uint4*>(k + off), r < L);
-        const uint4 qv = mask4(*reinterpret_cast<const uint4*>(q + off), r < L);
-        *reinterpret_cast<uint4*>(&sm.in.Kr[r][c8]) = kv;
-        *reinterpret_cast<uint4*>(&sm.in.Qr[r][c8]) = qv;
-        const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+        kv[u] = *reinterpret_cast<const u32x4*>(k + off);
+        qv[u] = *reinterpret_cast<const u32x4*>(q + off);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = (tid + NT * u) >> 4;
+        const int c8 = (tid & 15) * 8;
+        const uint32_t m = (r < L) ? 0xffffffffu : 0u;
+        const u32x4 kx = kv[u] & m, qx = qv[u] & m;
+        *reinterpret_cast<u32x4*>(&sm.in.Kr[r][c8]) = kx;
+        *reinterpret_cast<u32x4*>(&sm.in.Qr[r][c8]) = qx;
         float sk = 0.f, sq = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xffff0000u);
-            const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xffff0000u);
+            const float k0 = __uint_as_float(kx[e] << 16), k1 = __uint_as_float(kx[e] & 0xffff0000u);
+            const float q0 = __uint_as_float(qx[e] << 16), q1 = __uint_as_float(qx[e] & 0xffff0000u);
             sk += k0 * k0 + k1 * k1;
             sq += q0 * q0 + q1 * q1;
         }
-        sk = group_sum<16>(sk);
-        sq = group_sum<16>(sq);
+        sk = row16_sum(sk);
+        sq = row16_sum(sq);
         if ((lane & 15) == 0) {
             sm.rk[r] = l2norm ? inv_l2(sk) : 1.f;
             sm.rq[r] = l2norm ? inv_l2(sq) : 1.f;
