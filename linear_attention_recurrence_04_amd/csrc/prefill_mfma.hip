@@ -453,7 +453,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ch
 //    the bf16 state and Delta operands the state waves leave in LDS, and the
 //    output stores;
 //  * four loader waves: direct global -> LDS loads of the next chunk's inputs
-//    into double-buffered LDS.
+//    into double-buffered LDS, and cache-line touches of a chunk further
+//    ahead.
 // All eight meet at one barrier per chunk.
 // ===========================================================================
 
@@ -486,12 +487,21 @@ struct ScanSmem {
     bf16x8 Sx[2][NSTRIP][4][64];   // bf16 state operands (per strip, k step, lane)
     bf16x8 Dx[2][NSTRIP][2][64];   // Delta operands
     uint16_t Os[2][C][OS];         // output tiles, transposed to rows for 16-byte stores
+    uint32_t sink[LWAVES][64];     // landing area of the cache-line touches
 };
 
 // direct 16-byte load of one lane into LDS at base + 16 * lane (base wave-uniform)
 __device__ __forceinline__ void lds_load16(const void* g, void* lds_base) {
     __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
 }
+// 4-byte direct load: used to touch cache lines ahead of their use
+__device__ __forceinline__ void lds_load4(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(g, lds_base, 4, 0, 0);
+}
+// s_waitcnt immediate that waits until at most n vector memory operations are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt fields at their maximum, i.e. not waited for)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // transposed 4 x 16-bit read: within each 16 lanes, lane i receives element
 // i & 3 of the 8-byte pieces addressed by lanes (i >> 2) + 4j, j = 0..3
@@ -588,11 +598,46 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
             }
             load_gates(rec, B.gate);
         };
+        // Cache-line touches (4-byte loads into a scratch row of LDS) of the
+        // chunk TOUCH_AHEAD chunks ahead, so that its direct loads find the
+        // lines in L2 instead of waiting on HBM.  Each line is touched by one
+        // workgroup of those that share it: k and q lines by the first column
+        // block of the key head's first value head, the T, P and gate record
+        // by the head's first column block, v lines (128 bytes = two column
+        // blocks) by the even column blocks.  A wave touches two sets of
+        // lines or none.
+        constexpr int TOUCH_AHEAD = 3;
+        const bool first_block = (j0 == 0);
+        bool toucher;
+        if (lw == 0) toucher = first_block;
+        else if (lw == 1) toucher = (j0 % 64) == 0;
+        else toucher = first_block && (h % (Hv / Hk)) == 0;
+        auto touch = [&](int chunk) __attribute__((always_inline)) {
+            const int t0 = chunk * C;
+            const int row = t0 + min(lane, T - t0 - 1);
+            uint32_t* sink = sm.sink[lw];
+            const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;   // 138 lines of 128 bytes
+            if (lw == 0) {
+                lds_load4(rec + 128 * lane, sink);
+                lds_load4(rec + 128 * (64 + lane), sink);
+            } else if (lw == 1) {
+                lds_load4(vbase + (size_t)row * rowv, sink);
+                lds_load4(first_block ? rec + 128 * min(128 + lane, WS_REC / 128 - 1)
+                                      : reinterpret_cast<const unsigned char*>(vbase + (size_t)row * rowv), sink);
+            } else {
+                const bf16_t* base = (lw == 2) ? kbase : qbase;
+                lds_load4(base + (size_t)row * rowk, sink);
+                lds_load4(base + (size_t)row * rowk + 64, sink);
+            }
+        };
+        constexpr int NTOUCH = 2;
         // iteration c: the state waves work on chunk c and the output waves on
         // chunk c - 1; load the q-side inputs of chunk c and the k-side inputs
         // of chunk c + 1.  Loads of the last chunk (k side first) come after
         // every load of the earlier chunks, so the offsets switch to its
         // clamped rows once.
+        if (toucher)
+            for (int c = 1; c <= TOUCH_AHEAD && c < NTc; ++c) touch(c);
         if (NTc == 1) set_offsets(T - 1);
         load_k(0, 0);
         __builtin_amdgcn_s_waitcnt(0);
@@ -603,8 +648,20 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 if (c + 1 == NTc - 1) set_offsets(T - (NTc - 1) * C - 1);
                 load_k(c + 1, (c + 1) & 1);
             }
-            __builtin_amdgcn_s_waitcnt(0);   // this iteration's loads are in LDS
-            __syncthreads();
+            if (toucher && c + TOUCH_AHEAD < NTc) {
+                // vector memory operations complete in issue order: waiting
+                // until only the touches are outstanding waits for the loads
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                touch(c + TOUCH_AHEAD);
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(NTOUCH));
+            } else {
+                __builtin_amdgcn_s_waitcnt(0);   // this iteration's loads are in LDS
+            }
+            // a plain barrier: a fenced one would also wait for the touches
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
         }
         return;
     }
