@@ -87,7 +87,7 @@ typedef struct {
  * possible).  Returns 0 also for an invalid problem; gdn_chunk_prefill reports
  * the error.  The caller allocates the workspace; its contents need no
  * initialisation and are meaningless after the call.  The bf16 MFMA path
- * ("mfma_bf16" below) needs 17664 bytes per (sequence, value head, chunk of
+ * ("mfma_bf16" below) needs 13568 bytes per (sequence, value head, chunk of
  * 64 tokens): the chunk's triangular inverse, masked Q K^T and gate vectors,
  * computed for all chunks in parallel before the serial pass.
  */

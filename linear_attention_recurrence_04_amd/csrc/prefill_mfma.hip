@@ -57,13 +57,15 @@ constexpr int NT = 256;     // threads per workgroup (both kernels)
 constexpr int SK = D + 8;   // padded row stride (elements) of [64][128] bf16 tiles
 constexpr int SC = C + 8;   // padded row stride of [*][64] bf16 tiles
 
-// Workspace record per (b, value head, chunk): T and P (64x64 bf16, operand
-// order) and the gate vectors (fp32): grk, wrk, grq, beta, Gamma_C.
+// Workspace record per (b, value head, chunk): T and P (64x64 bf16 in
+// operand order, compact images: see imgc) and the gate vectors (fp32):
+// grk, wrk, beta, Gamma_C (read with k) and grq (read with q).
+constexpr int IMG_BYTES = (32 * 32 + 32 * 64) * 2;   // 6144
 constexpr int WS_T = 0;
-constexpr int WS_P = C * C * 2;
-constexpr int WS_G = 2 * C * C * 2;
-constexpr int NGATE = 5;
-constexpr int WS_REC = WS_G + NGATE * C * 4;   // 17664 bytes
+constexpr int WS_P = IMG_BYTES;
+constexpr int WS_G = 2 * IMG_BYTES;
+constexpr int WS_GQ = WS_G + 4 * C * 4;
+constexpr int WS_REC = WS_GQ + C * 4;               // 13568 bytes
 
 // Contraction-index order inside each 32-wide k step.  A pair of accumulator
 // tiles (rows 32ks.., 32ks+16..) gives lane (g, n) the rows {4g..4g+3} and
@@ -129,12 +131,21 @@ __device__ __forceinline__ void tile_of(int idx, int& a, int& b) {
 __host__ __device__ constexpr int tile_a(int idx) { return (idx >= 1) + (idx >= 3) + (idx >= 6); }
 __host__ __device__ constexpr int tile_b(int idx) { return idx - (tile_a(idx) * (tile_a(idx) + 1)) / 2; }
 
-// The [rows][64] bf16 images (T, P, k transposed) are read by the scan as
-// 16-byte MFMA operands; chunk c (logical columns 8c..8c+7) of row r is stored
-// at chunk c ^ ((r >> 1) & 7), so that the 16 rows an operand read touches
-// hit distinct LDS banks.  Element position of logical column L in row r:
-__host__ __device__ constexpr int img64(int r, int L) {
-    return r * 64 + 8 * ((L >> 3) ^ ((r >> 1) & 7)) + (L & 7);
+// T and P are read by the scan as 16-byte MFMA operands: rows 0..31 only at
+// logical columns 0..31 (their first k step; the rest is zero), rows 32..63
+// at all 64.  The image keeps just those: rows 0..31 as 64-byte rows, rows
+// 32..63 as 128-byte rows after them.  Chunk c (logical columns 8c..8c+7) of
+// row r sits at chunk c ^ 2((r >> 2) & 1) in the short rows and at
+// c ^ ((r >> 1) & 7) in the long ones, so that the 16 rows an operand read
+// touches fall in distinct LDS banks.  Element position of logical column L
+// in row r (L < 32 when r < 32):
+__host__ __device__ constexpr int imgc(int r, int L) {
+    return r < 32 ? r * 32 + 8 * ((L >> 3) ^ (((r >> 2) & 1) << 1)) + (L & 7)
+                  : 1024 + (r - 32) * 64 + 8 * ((L >> 3) ^ ((r >> 1) & 7)) + (L & 7);
+}
+// the same position in 16-byte units for logical chunk c
+__host__ __device__ constexpr int imgq(int r, int c) {
+    return r < 32 ? r * 4 + (c ^ (((r >> 2) & 1) << 1)) : 128 + (r - 32) * 8 + (c ^ ((r >> 1) & 7));
 }
 
 // ===========================================================================
@@ -215,11 +226,11 @@ __device__ __forceinline__ void gate_tiles(PrepSmem& sm, const f32x4 (&gram)[5],
             }
             if (is_qk) {
                 const int q4 = 4 * bb + g;   // physical 4-group of s
-                *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (q4 >> 3) + kperm(q4 & 7))) = pack4(val);
+                *reinterpret_cast<s16x4*>(Pg + imgc(r, 32 * (q4 >> 3) + kperm(q4 & 7))) = pack4(val);
                 if (a == bb && (a == 0 || a == 2)) {  // upper neighbour read by the scan: zero
                     const int qz = q4 + 4;
                     const s16x4 z = {0, 0, 0, 0};
-                    *reinterpret_cast<s16x4*>(Pg + img64(r, 32 * (qz >> 3) + kperm(qz & 7))) = z;
+                    *reinterpret_cast<s16x4*>(Pg + imgc(r, 32 * (qz >> 3) + kperm(qz & 7))) = z;
                 }
             } else if (a == bb) {
 #pragma unroll
@@ -344,9 +355,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ch
             float* gp = reinterpret_cast<float*>(ws + (((size_t)b * Hv + h) * NTc + chunk) * WS_REC + WS_G);
             gp[0 * C + lane] = Gm * rkv;
             gp[1 * C + lane] = exp_hw(total - x) * rkv;
-            gp[2 * C + lane] = Gm * sm.rq[lane];
-            gp[3 * C + lane] = btv;
-            gp[4 * C + lane] = exp_hw(total);
+            gp[2 * C + lane] = btv;
+            gp[3 * C + lane] = exp_hw(total);
+            gp[4 * C + lane] = Gm * sm.rq[lane];
         }
         __syncthreads();   // k and q rows are dead from here: their space holds A and T
 
@@ -437,9 +448,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ch
                 const int r = e >> 4;
                 const int Qg = e & 15;
                 const int bi = r >> 4, bj = Qg >> 2;
+                if (r < 32 && Qg >= 8) continue;   // not in the image (zero)
                 uint2 val = make_uint2(0u, 0u);
                 if (bj <= bi) val = *reinterpret_cast<const uint2*>(&sm.tri.Tl[hh][tl_idx(bi, bj)][r & 15][4 * (Qg & 3)]);
-                *reinterpret_cast<uint2*>(Tg + img64(r, 32 * (Qg >> 3) + kperm(Qg & 7))) = val;
+                *reinterpret_cast<uint2*>(Tg + imgc(r, 32 * (Qg >> 3) + kperm(Qg & 7))) = val;
             }
         }
     }
@@ -472,14 +484,14 @@ __host__ __device__ constexpr int swz(int r) { return ((r & 3) << 2) | ((r >> 2)
 
 struct KSet {              // state-wave inputs of one chunk
     uint4 K[C * 16];       // k rows, swizzled
-    uint4 T[C * 8];        // T image
+    uint4 T[IMG_BYTES / 16];   // T image
     uint4 V[C * 4];        // v rows of the 32 columns: chunk c of row s at c ^ ((s >> 2) & 3)
-    float gate[NGATE * C]; // grk, wrk, grq, beta, Gamma_C
+    float gate[4 * C];     // grk, wrk, beta, Gamma_C
 };
 struct QSet {              // output-wave inputs of one chunk
     uint4 Q[C * 16];       // q rows, swizzled
-    uint4 P[C * 8];        // P image
-    float gate[NGATE * C];
+    uint4 P[IMG_BYTES / 16];   // P image
+    float gate[C];         // grq
 };
 struct ScanSmem {
     KSet ks[2];
@@ -547,7 +559,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
         const int lw = w - 2 * NSTRIP;
         // per-lane byte offsets inside a chunk (rows clamped to `last`), so
         // that each k, q or v load is a uniform base plus a 32-bit lane offset
-        constexpr int NKB = 16 / LWAVES, NVB = 4 / LWAVES, NRB = 8 / LWAVES;
+        constexpr int NKB = 16 / LWAVES, NVB = 4 / LWAVES, NRB = (IMG_BYTES / 1024 + LWAVES - 1) / LWAVES;
         uint32_t offk[NKB], offv[NVB];
         auto set_offsets = [&](int last) __attribute__((always_inline)) {
 #pragma unroll
@@ -562,11 +574,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
             }
         };
         set_offsets(C - 1);
-        auto load_gates = [&](const unsigned char* rec, float* gate) __attribute__((always_inline)) {
-            // 1280 bytes: one full 1 KiB block and 16 lanes of a second
-            if (lw == 0) lds_load16(rec + WS_G + 16 * lane, gate);
-            else if (lw == 1 && lane < 16) lds_load16(rec + WS_G + 1024 + 16 * lane, gate + 256);
-        };
+
         auto load_k = [&](int chunk, int slot) __attribute__((always_inline)) {
             KSet& B = sm.ks[slot];
             const int t0 = chunk * C;
@@ -576,13 +584,13 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
 #pragma unroll
             for (int u = 0; u < NKB; ++u) lds_load16(kc + offk[u], &B.K[64 * (lw + LWAVES * u)]);
 #pragma unroll
-            for (int u = 0; u < NRB; ++u) {
+            for (int u = 0; u < NRB; ++u) {            // 6 blocks of 1 KiB
                 const int blk = lw + LWAVES * u;
-                lds_load16(rec + WS_T + 1024 * blk + 16 * lane, &B.T[64 * blk]);
+                if (blk < IMG_BYTES / 1024) lds_load16(rec + WS_T + 1024 * blk + 16 * lane, &B.T[64 * blk]);
             }
 #pragma unroll
             for (int u = 0; u < NVB; ++u) lds_load16(vc + offv[u], &B.V[64 * (lw + LWAVES * u)]);
-            load_gates(rec, B.gate);
+            if (lw == 2) lds_load16(rec + WS_G + 16 * lane, B.gate);   // 1 KiB
         };
         auto load_q = [&](int chunk, int slot) __attribute__((always_inline)) {
             QSet& B = sm.qs[slot];
@@ -594,9 +602,9 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
 #pragma unroll
             for (int u = 0; u < NRB; ++u) {
                 const int blk = lw + LWAVES * u;
-                lds_load16(rec + WS_P + 1024 * blk + 16 * lane, &B.P[64 * blk]);
+                if (blk < IMG_BYTES / 1024) lds_load16(rec + WS_P + 1024 * blk + 16 * lane, &B.P[64 * blk]);
             }
-            load_gates(rec, B.gate);
+            if (lw == 3 && lane < 16) lds_load16(rec + WS_GQ + 16 * lane, B.gate);   // 256 bytes
         };
         // Cache-line touches (4-byte loads into a scratch row of LDS) of the
         // chunk TOUCH_AHEAD chunks ahead, so that its direct loads find the
@@ -616,14 +624,13 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
             const int t0 = chunk * C;
             const int row = t0 + min(lane, T - t0 - 1);
             uint32_t* sink = sm.sink[lw];
-            const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;   // 138 lines of 128 bytes
+            const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;   // 106 lines of 128 bytes
             if (lw == 0) {
                 lds_load4(rec + 128 * lane, sink);
-                lds_load4(rec + 128 * (64 + lane), sink);
+                lds_load4(rec + 128 * min(64 + lane, WS_REC / 128 - 1), sink);
             } else if (lw == 1) {
                 lds_load4(vbase + (size_t)row * rowv, sink);
-                lds_load4(first_block ? rec + 128 * min(128 + lane, WS_REC / 128 - 1)
-                                      : reinterpret_cast<const unsigned char*>(vbase + (size_t)row * rowv), sink);
+                lds_load4(vbase + (size_t)row * rowv + 32, sink);   // same line: keeps two per toucher
             } else {
                 const bf16_t* base = (lw == 2) ? kbase : qbase;
                 lds_load4(base + (size_t)row * rowk, sink);
@@ -670,7 +677,6 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     const int strip = (w < NSTRIP) ? w : w - NSTRIP;
     const int jw = j0 + SW * strip;      // first state column of the strip
     const int sn = swz(n);               // swizzle of rows 16i + n
-    const int sw = n >> 1;               // image swizzle of rows 16i + n
 
     // ======================= state waves =======================
     if (w < NSTRIP) {
@@ -699,7 +705,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int s0 = 16 * i + 4 * g;
-                    btv[i] = *reinterpret_cast<const f32x4*>(&B.gate[3 * C + s0]);
+                    btv[i] = *reinterpret_cast<const f32x4*>(&B.gate[2 * C + s0]);
                     grk[i] = *reinterpret_cast<const f32x4*>(&B.gate[0 * C + s0]);
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
@@ -738,9 +744,9 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 // ---- T operands (needed next), issued before the X arithmetic
                 bf16x8 at0[4], at1[2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) at0[i] = __builtin_bit_cast(bf16x8, B.T[(16 * i + n) * 8 + (g ^ sw)]);
-                at1[0] = __builtin_bit_cast(bf16x8, B.T[(32 + n) * 8 + ((4 + g) ^ sw)]);
-                at1[1] = __builtin_bit_cast(bf16x8, B.T[(48 + n) * 8 + ((4 + g) ^ sw)]);
+                for (int i = 0; i < 4; ++i) at0[i] = __builtin_bit_cast(bf16x8, B.T[imgq(16 * i + n, g)]);
+                at1[0] = __builtin_bit_cast(bf16x8, B.T[imgq(32 + n, 4 + g)]);
+                at1[1] = __builtin_bit_cast(bf16x8, B.T[imgq(48 + n, 4 + g)]);
                 __builtin_amdgcn_sched_barrier(0);
                 // ---- X = beta (V - Gamma rk K S)
                 f32x4 X[4];
@@ -771,7 +777,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 const f32x4 whi0 = *reinterpret_cast<const f32x4*>(&B.gate[C + 16 + 4 * g]);
                 const f32x4 wlo1 = *reinterpret_cast<const f32x4*>(&B.gate[C + 32 + 4 * g]);
                 const f32x4 whi1 = *reinterpret_cast<const f32x4*>(&B.gate[C + 48 + 4 * g]);
-                const float GC = B.gate[4 * C];
+                const float GC = B.gate[3 * C];
                 __builtin_amdgcn_sched_barrier(0);
                 // ---- Delta = T X (T lower triangular: row tile i needs k steps <= i/2)
                 f32x4 Dl[4];
@@ -836,14 +842,14 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
             }
             bf16x8 ap0[4], ap1[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ap0[i] = __builtin_bit_cast(bf16x8, B.P[(16 * i + n) * 8 + (g ^ sw)]);
-            ap1[0] = __builtin_bit_cast(bf16x8, B.P[(32 + n) * 8 + ((4 + g) ^ sw)]);
-            ap1[1] = __builtin_bit_cast(bf16x8, B.P[(48 + n) * 8 + ((4 + g) ^ sw)]);
+            for (int i = 0; i < 4; ++i) ap0[i] = __builtin_bit_cast(bf16x8, B.P[imgq(16 * i + n, g)]);
+            ap1[0] = __builtin_bit_cast(bf16x8, B.P[imgq(32 + n, 4 + g)]);
+            ap1[1] = __builtin_bit_cast(bf16x8, B.P[imgq(48 + n, 4 + g)]);
             const bf16x8 DB0 = sm.Dx[cc & 1][strip][0][lane];
             const bf16x8 DB1 = sm.Dx[cc & 1][strip][1][lane];
             f32x4 grq[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) grq[i] = *reinterpret_cast<const f32x4*>(&B.gate[2 * C + 16 * i + 4 * g]);
+            for (int i = 0; i < 4; ++i) grq[i] = *reinterpret_cast<const f32x4*>(&B.gate[16 * i + 4 * g]);
             // ---- O = Gamma rq Q S + P Delta
             f32x4 O4[4];
 #pragma unroll
