@@ -494,11 +494,11 @@ struct QSet {              // output-wave inputs of one chunk
     float gate[C];         // grq
 };
 struct ScanSmem {
-    KSet ks[2];
-    QSet qs[2];
+    KSet ks[3];                    // k side: chunk c in ks[c % 3], loaded two chunks ahead
+    QSet qs[2];                    // q side: chunk c in qs[c % 2], loaded one chunk ahead
     bf16x8 Sx[2][NSTRIP][4][64];   // bf16 state operands (per strip, k step, lane)
     bf16x8 Dx[2][NSTRIP][2][64];   // Delta operands
-    uint16_t Os[2][C][OS];         // output tiles, transposed to rows for 16-byte stores
+    uint16_t Os[C][OS];            // output tile, transposed to rows for 16-byte stores
     uint32_t sink[LWAVES][64];     // landing area of the cache-line touches
 };
 
@@ -558,24 +558,38 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     if (w >= 2 * NSTRIP) {
         const int lw = w - 2 * NSTRIP;
         // per-lane byte offsets inside a chunk (rows clamped to `last`), so
-        // that each k, q or v load is a uniform base plus a 32-bit lane offset
+        // that each k, q or v load is a uniform base plus a 32-bit lane offset;
+        // the k side and the q side switch to the last chunk's rows separately
         constexpr int NKB = 16 / LWAVES, NVB = 4 / LWAVES, NRB = (IMG_BYTES / 1024 + LWAVES - 1) / LWAVES;
-        uint32_t offk[NKB], offv[NVB];
-        auto set_offsets = [&](int last) __attribute__((always_inline)) {
+        uint32_t offk[NKB], offq[NKB], offv[NVB];
+        auto kq_offsets = [&](uint32_t (&off)[NKB], int last) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < NKB; ++u) {            // k / q: 16 blocks of 4 rows
                 const int r = 4 * (lw + LWAVES * u) + (lane >> 4);
-                offk[u] = 2u * (uint32_t)(min(r, last) * rowk + 8 * ((lane & 15) ^ swz(r)));
+                off[u] = 2u * (uint32_t)(min(r, last) * rowk + 8 * ((lane & 15) ^ swz(r)));
             }
+        };
+        auto v_offsets = [&](int last) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < NVB; ++u) {            // v: 4 blocks of 16 rows
                 const int s2 = 16 * (lw + LWAVES * u) + (lane >> 2);
                 offv[u] = 2u * (uint32_t)(min(s2, last) * rowv + 8 * ((lane & 3) ^ ((s2 >> 2) & 3)));
             }
         };
-        set_offsets(C - 1);
+        const int last_rows = T - (NTc - 1) * C - 1;   // last row of the last chunk
+        kq_offsets(offk, C - 1);
+        kq_offsets(offq, C - 1);
+        v_offsets(C - 1);
 
+        // The k side of a chunk is 7 direct loads per loader wave (k 4, T 2
+        // or 1, v 1, gates 1 on one wave; the fourth wave repeats its last k
+        // block), so that one wait count fits every wave.
+        constexpr int NKLOADS = 7;
         auto load_k = [&](int chunk, int slot) __attribute__((always_inline)) {
+            if (chunk == NTc - 1) {   // the last chunk: clamp its rows
+                kq_offsets(offk, last_rows);
+                v_offsets(last_rows);
+            }
             KSet& B = sm.ks[slot];
             const int t0 = chunk * C;
             const unsigned char* kc = reinterpret_cast<const unsigned char*>(kbase + (size_t)t0 * rowk);
@@ -591,14 +605,16 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
 #pragma unroll
             for (int u = 0; u < NVB; ++u) lds_load16(vc + offv[u], &B.V[64 * (lw + LWAVES * u)]);
             if (lw == 2) lds_load16(rec + WS_G + 16 * lane, B.gate);   // 1 KiB
+            if (lw == 3) lds_load16(kc + offk[NKB - 1], &B.K[64 * (lw + LWAVES * (NKB - 1))]);   // count filler
         };
         auto load_q = [&](int chunk, int slot) __attribute__((always_inline)) {
+            if (chunk == NTc - 1) kq_offsets(offq, last_rows);
             QSet& B = sm.qs[slot];
             const int t0 = chunk * C;
             const unsigned char* qc = reinterpret_cast<const unsigned char*>(qbase + (size_t)t0 * rowk);
             const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;
 #pragma unroll
-            for (int u = 0; u < NKB; ++u) lds_load16(qc + offk[u], &B.Q[64 * (lw + LWAVES * u)]);
+            for (int u = 0; u < NKB; ++u) lds_load16(qc + offq[u], &B.Q[64 * (lw + LWAVES * u)]);
 #pragma unroll
             for (int u = 0; u < NRB; ++u) {
                 const int blk = lw + LWAVES * u;
@@ -639,33 +655,33 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
         };
         constexpr int NTOUCH = 2;
         // iteration c: the state waves work on chunk c and the output waves on
-        // chunk c - 1; load the q-side inputs of chunk c and the k-side inputs
-        // of chunk c + 1.  Loads of the last chunk (k side first) come after
-        // every load of the earlier chunks, so the offsets switch to its
-        // clamped rows once.
+        // chunk c - 1; load the q side of chunk c, then the k side of chunk
+        // c + 2, then the touches.  Operations complete in issue order, so
+        // waiting until only the k loads and touches of this iteration are
+        // outstanding covers the q side of chunk c and the k side of chunk
+        // c + 1 (issued an iteration ago): what the next iteration reads.
         if (toucher)
             for (int c = 1; c <= TOUCH_AHEAD && c < NTc; ++c) touch(c);
-        if (NTc == 1) set_offsets(T - 1);
         load_k(0, 0);
+        if (NTc > 1) load_k(1, 1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int c = 0; c <= NTc; ++c) {
             if (c < NTc) load_q(c, c & 1);
-            if (c + 1 < NTc) {
-                if (c + 1 == NTc - 1) set_offsets(T - (NTc - 1) * C - 1);
-                load_k(c + 1, (c + 1) & 1);
-            }
-            if (toucher && c + TOUCH_AHEAD < NTc) {
-                // vector memory operations complete in issue order: waiting
-                // until only the touches are outstanding waits for the loads
-                asm volatile("" ::: "memory");
-                __builtin_amdgcn_sched_barrier(0);
-                touch(c + TOUCH_AHEAD);
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(NTOUCH));
-            } else {
-                __builtin_amdgcn_s_waitcnt(0);   // this iteration's loads are in LDS
-            }
-            // a plain barrier: a fenced one would also wait for the touches
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            const bool kload = c + 2 < NTc;
+            if (kload) load_k(c + 2, (c + 2) % 3);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            const bool tload = toucher && c + TOUCH_AHEAD < NTc;
+            if (tload) touch(c + TOUCH_AHEAD);
+            if (kload && tload) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NKLOADS + NTOUCH));
+            else if (kload) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NKLOADS));
+            else if (tload) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NTOUCH));
+            else __builtin_amdgcn_s_waitcnt(0);
+            // a plain barrier: a fenced one would also wait for the loads
+            // and touches still in flight
             asm volatile("" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
@@ -696,7 +712,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
         }
         for (int c = 0; c <= NTc; ++c) {
             if (c < NTc) {
-                const KSet& B = sm.ks[c & 1];
+                const KSet& B = sm.ks[c % 3];
                 // ---- gate vectors, v values, the K operands of the first k step
                 f32x4 btv[4], grk[4];
                 uint32_t vv[4][4];
@@ -856,7 +872,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
             for (int i = 0; i < 4; ++i) O4[i] = mfma32(ap0[i], DB0, grq[i] * QS[i]);
             O4[2] = mfma32(ap1[0], DB1, O4[2]);
             O4[3] = mfma32(ap1[1], DB1, O4[3]);
-            uint16_t (*Ot)[OS] = sm.Os[cc & 1];
+            uint16_t (*Ot)[OS] = sm.Os;   // each output wave reads back only its own columns
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
