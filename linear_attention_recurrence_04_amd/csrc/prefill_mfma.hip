@@ -713,33 +713,27 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
         for (int c = 0; c <= NTc; ++c) {
             if (c < NTc) {
                 const KSet& B = sm.ks[c % 3];
-                // ---- gate vectors, v values, the K operands of the first k step
-                f32x4 btv[4], grk[4];
-                uint32_t vv[4][4];
-                const unsigned char* Vb = reinterpret_cast<const unsigned char*>(B.V);
-                const int vc = 2 * strip + (n >> 3);      // 16-byte chunk of this lane's column
+                // ---- K operands of the first k step, then the bf16 state
+                //      operands (also left in LDS for the output wave)
+                bf16x8 ak[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int s0 = 16 * i + 4 * g;
-                    btv[i] = *reinterpret_cast<const f32x4*>(&B.gate[2 * C + s0]);
-                    grk[i] = *reinterpret_cast<const f32x4*>(&B.gate[0 * C + s0]);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        vv[i][t] = *reinterpret_cast<const uint16_t*>(Vb + (s0 + t) * 64 + 16 * (vc ^ g) + 2 * (n & 7));
-                }
+                for (int i = 0; i < 4; ++i) ak[i] = __builtin_bit_cast(bf16x8, B.K[(16 * i + n) * 16 + (g ^ sn)]);
                 bf16x8 SB[4];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     SB[ks] = pack8(S[2 * ks], S[2 * ks + 1]);
                     sm.Sx[c & 1][strip][ks][lane] = SB[ks];   // for the output wave
                 }
+                // ---- K S: k step outer, 4 independent accumulators inner.  The
+                //      v values, Gamma rk, beta and the T operands, needed only
+                //      after it, are read behind the operands of the later k steps.
                 f32x4 KS[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) KS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                bf16x8 ak[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ak[i] = __builtin_bit_cast(bf16x8, B.K[(16 * i + n) * 16 + (g ^ sn)]);
-                // ---- K S: k step outer, 4 independent accumulators inner
+                s16x4 vt[4];
+                f32x4 btv[4], grk[4];
+                bf16x8 at0[4], at1[2];   // T operands
+                const unsigned char* Vb = reinterpret_cast<const unsigned char*>(B.V);
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     bf16x8 nk[4];
@@ -747,6 +741,28 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
                             nk[i] = __builtin_bit_cast(bf16x8, B.K[(16 * i + n) * 16 + ((4 * (ks + 1) + g) ^ sn)]);
+                    }
+                    if (ks == 1) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            // transposed read: lane (g, n) receives v rows 16i + 4g + j,
+                            // j = 0..3, at column 16 strip + n; it addresses row
+                            // 16i + 4g + (n >> 2), columns 16 strip + 4 (n & 3) .. + 3
+                            const int sr = 16 * i + 4 * g + (n >> 2);
+                            vt[i] = ld_tr4(Vb + sr * 64 + 16 * ((2 * strip + ((n >> 1) & 1)) ^ g) + 8 * (n & 1));
+                            grk[i] = *reinterpret_cast<const f32x4*>(&B.gate[0 * C + 16 * i + 4 * g]);
+                        }
+                    }
+                    if (ks == 2) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            btv[i] = *reinterpret_cast<const f32x4*>(&B.gate[2 * C + 16 * i + 4 * g]);
+                            at0[i] = __builtin_bit_cast(bf16x8, B.T[imgq(16 * i + n, g)]);
+                        }
+                    }
+                    if (ks == 3) {
+                        at1[0] = __builtin_bit_cast(bf16x8, B.T[imgq(32 + n, 4 + g)]);
+                        at1[1] = __builtin_bit_cast(bf16x8, B.T[imgq(48 + n, 4 + g)]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -757,20 +773,13 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                         for (int i = 0; i < 4; ++i) ak[i] = nk[i];
                     }
                 }
-                // ---- T operands (needed next), issued before the X arithmetic
-                bf16x8 at0[4], at1[2];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) at0[i] = __builtin_bit_cast(bf16x8, B.T[imgq(16 * i + n, g)]);
-                at1[0] = __builtin_bit_cast(bf16x8, B.T[imgq(32 + n, 4 + g)]);
-                at1[1] = __builtin_bit_cast(bf16x8, B.T[imgq(48 + n, 4 + g)]);
-                __builtin_amdgcn_sched_barrier(0);
                 // ---- X = beta (V - Gamma rk K S)
                 f32x4 X[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
-                        X[i][t] = btv[i][t] * (__uint_as_float(vv[i][t] << 16) - grk[i][t] * KS[i][t]);
+                        X[i][t] = btv[i][t] * (__uint_as_float((uint32_t)(uint16_t)vt[i][t] << 16) - grk[i][t] * KS[i][t]);
                 const bf16x8 XB0 = pack8(X[0], X[1]);
                 const bf16x8 XB1 = pack8(X[2], X[3]);
                 // ---- k^T operands of the state update, read transposed from the
