@@ -5,7 +5,9 @@ One "step" is one chunked-prefill call of the 27B-shaped workload
 fp32 gates and state, chunk 64).  ``value`` is prefill tokens/s.  The decode
 half of the metric (B=64 sequences, same heads, one token per step for 1000
 steps, fp32 state updated in place) is timed in the same run and reported
-under "decode" as state-update HBM GB/s and tokens/s.
+under "decode" as state-update HBM GB/s and tokens/s.  The same prefill call
+storing a state checkpoint every 512 tokens (gdn_chunk_prefill_ckpt) is timed
+too and reported under "checkpoints".
 
 Inputs are seeded synthetic tensors already resident in HBM when the timed
 region starts.  Kernel time comes from HIP events recorded on the stream the
@@ -114,7 +116,9 @@ def time_stream(torch, fn, steps: int):
     return start.elapsed_time(stop)  # ms
 
 
-def bench_prefill(torch, gdn, p, steps, warmup):
+def bench_prefill(torch, gdn, p, steps, warmup, ckpt_every: int = 0):
+    """ms per prefill call; with ckpt_every > 0 the call also stores the state
+    every ckpt_every tokens (gdn_chunk_prefill_ckpt)."""
     log(f"prefill workload {p.name}: generating inputs")
     inp = gi.make_prefill(p, 0)
     dev = {n: torch.from_numpy(inp[n]).cuda() for n in ("q", "k", "v", "log_g", "beta", "h0")}
@@ -127,14 +131,24 @@ def bench_prefill(torch, gdn, p, steps, warmup):
     ws_bytes = gdn.gdn_chunk_prefill_workspace_bytes(prob)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
-    def call():
-        gdn.gdn_chunk_prefill(dev["q"], dev["k"], dev["v"], dev["log_g"], dev["beta"], dev["h0"],
-                              chunk=p.chunk, out=out, hT=hT, workspace=ws)
+    if ckpt_every:
+        nck = -(-p.T // ckpt_every)
+        ck = torch.empty((p.B, nck, p.Hv, p.dk, p.dv), dtype=torch.float32, device="cuda")
+
+        def call():
+            gdn.gdn_chunk_prefill_ckpt(dev["q"], dev["k"], dev["v"], dev["log_g"], dev["beta"],
+                                       dev["h0"], ckpt_every=ckpt_every, chunk=p.chunk, out=out,
+                                       hT=hT, h_ckpt=ck, workspace=ws)
+    else:
+        def call():
+            gdn.gdn_chunk_prefill(dev["q"], dev["k"], dev["v"], dev["log_g"], dev["beta"],
+                                  dev["h0"], chunk=p.chunk, out=out, hT=hT, workspace=ws)
 
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    log(f"prefill: timing {steps} steps")
+    log(f"prefill{' with checkpoints every %d' % ckpt_every if ckpt_every else ''}: "
+        f"timing {steps} steps")
     ms = time_stream(torch, call, steps)
     return ms / steps, prob
 
@@ -259,6 +273,19 @@ def main():
             "avg_launch_us": round(ms * 1e3, 2), "source_hash": src,
         }
         log(f"prefill: {ms:.3f} ms/call, {result['value']:.0f} tok/s, {gbps:.1f} GB/s, {tflops:.2f} TFLOP/s")
+        # the same call storing a state checkpoint every 512 tokens (32 slots)
+        every = 512
+        ms_c, _ = bench_prefill(torch, gdn, p, args.steps, args.warmup, ckpt_every=every)
+        nck = -(-p.T // every)
+        ck_bytes = p.B * nck * p.Hv * p.dk * p.dv * 4
+        result["checkpoints"] = {
+            "ckpt_every": every, "slots": nck, "slot_bytes_total": ck_bytes,
+            "ms_per_call": round(ms_c, 4), "overhead_ms": round(ms_c - ms, 4),
+            "tokens_per_s": round(p.B * p.T / (ms_c * 1e-3), 1),
+            "extra_write_GBps_over_overhead": (round(ck_bytes / ((ms_c - ms) * 1e-3) / 1e9, 1)
+                                               if ms_c > ms else None),
+        }
+        log(f"prefill with {nck} checkpoints: {ms_c:.3f} ms/call ({(ms_c - ms) * 1e3:+.1f} us)")
 
     if args.only in ("all", "decode"):
         ms_d = bench_decode(torch, gdn, d, args.decode_steps, min(args.warmup, 10) or 1)

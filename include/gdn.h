@@ -126,6 +126,36 @@ gdn_status gdn_chunk_prefill(const gdn_problem* problem,
                              void* hip_stream);
 
 /*
+ * gdn_chunk_prefill that also stores the recurrent state every ckpt_every
+ * tokens: the GDN checkpoint slots that hybrid prefix caching restores from.
+ * A reusable prefix of a hybrid DeltaNet/attention model needs a recurrent-
+ * state checkpoint at its end as well as attention KV hits ("Add Qwen3.6-27B
+ * hybrid DeltaNet/GQA contrib model and vLLM serving path", summary), and the
+ * serving path commits such checkpoints from chunked prefill into a bank of
+ * slots ("Qwen3.6: Fused DeltaNet Direct-Solve Follow-Up", sections "Hybrid
+ * APC Runtime", "Qwen Model Execution" and "Memory").
+ *
+ *   h_ckpt      [B, NCK, Hv, dk, dv] fp32, NCK = ceil(T / ckpt_every), written:
+ *               slot j holds the state after min((j + 1) * ckpt_every, T)
+ *               tokens of the sequence (the last slot therefore equals hT).
+ *               It may not overlap any other argument.  With T == 0 nothing
+ *               is written to it and it may be NULL.
+ *   ckpt_every  tokens between checkpoints: a positive multiple of the chunk
+ *               length the call runs with (problem->chunk, 0 meaning 64);
+ *               otherwise GDN_ERR_BAD_SHAPE.
+ * Every other argument, check and result is that of gdn_chunk_prefill (same
+ * workspace size).  A slot is bitwise the hT of a call that stops at its
+ * token, since both run the same chunks in the same order.
+ */
+gdn_status gdn_chunk_prefill_ckpt(const gdn_problem* problem,
+                                  const void* q, const void* k, const void* v,
+                                  const float* log_g, const float* beta,
+                                  const float* h0, float* hT, void* o,
+                                  float* h_ckpt, int32_t ckpt_every,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* hip_stream);
+
+/*
  * One decode step (one token per sequence) updating the state in place.
  *
  * Evaluates the five steps for a single token with one read and one write of

@@ -60,6 +60,9 @@ def lib():
     L.gdn_chunk_prefill_variant.argtypes = [pp]
     L.gdn_chunk_prefill.restype = ctypes.c_int
     L.gdn_chunk_prefill.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, vp, vp, sz, vp]
+    L.gdn_chunk_prefill_ckpt.restype = ctypes.c_int
+    L.gdn_chunk_prefill_ckpt.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, vp, fp, ctypes.c_int32,
+                                         vp, sz, vp]
     L.gdn_decode_step.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [pp, vp, vp, vp, fp, fp, fp, vp, vp]
     _lib = L
@@ -188,6 +191,51 @@ def gdn_chunk_prefill(q, k, v, log_g, beta, h0=None, *, chunk: int = 64,
                                  ws_bytes, _stream(stream))
     _check(st)
     return out, hT
+
+
+def gdn_chunk_prefill_ckpt(q, k, v, log_g, beta, h0=None, *, ckpt_every: int,
+                           chunk: int = 64, qk_l2norm: bool = True, q_scale: float = 1.0,
+                           out=None, hT=None, h_ckpt=None, workspace=None, stream=None):
+    """Chunked prefill that also stores the state every ``ckpt_every`` tokens.
+    Returns (o, hT, h_ckpt) with h_ckpt [B, ceil(T/ckpt_every), Hv, d, d] fp32:
+    slot j is the state after min((j+1) ckpt_every, T) tokens."""
+    torch = _torch()
+    _need(q, "q")
+    dt = _dtype_code(q)
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    _need(k, "k", q.dtype, q.shape)
+    _need(v, "v", q.dtype, (B, T, Hv, dv))
+    _need(log_g, "log_g", torch.float32, (B, T, Hv))
+    _need(beta, "beta", torch.float32, (B, T, Hv))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, Hv, dk, dv))
+    every = int(ckpt_every)
+    nck = -(-T // every) if every > 0 else 0
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(out, "out", q.dtype, (B, T, Hv, dv))
+    if hT is None:
+        hT = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=q.device)
+    else:
+        _need(hT, "hT", torch.float32, (B, Hv, dk, dv))
+    if h_ckpt is None:
+        h_ckpt = torch.empty((B, max(nck, 0), Hv, dk, dv), dtype=torch.float32, device=q.device)
+    else:
+        _need(h_ckpt, "h_ckpt", torch.float32, (B, nck, Hv, dk, dv))
+    prob = make_problem(B, T, Hk, Hv, dk, dv, chunk=chunk, dtype=dt, qk_l2norm=qk_l2norm,
+                        q_scale=q_scale)
+    need = gdn_chunk_prefill_workspace_bytes(prob)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ck_ptr = _ptr(h_ckpt) if h_ckpt.numel() else None
+    st = lib().gdn_chunk_prefill_ckpt(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(log_g), _ptr(beta), _ptr(h0), _ptr(hT), _ptr(out),
+                                      ck_ptr, every, _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st)
+    return out, hT, h_ckpt
 
 
 def gdn_decode_step(q, k, v, log_g, beta, state, *, qk_l2norm: bool = True,

@@ -104,20 +104,28 @@ size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* p) {
     return 0;  // the fp32 kernel keeps every intermediate on chip
 }
 
-gdn_status gdn_chunk_prefill(const gdn_problem* p, const void* q, const void* k, const void* v,
-                             const float* log_g, const float* beta, const float* h0, float* hT,
-                             void* o, void* workspace, size_t workspace_bytes, void* hip_stream) {
-    gdn_status st = check_problem(p, false);
-    if (st != GDN_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// gdn_chunk_prefill with optional checkpoints (h_ckpt == NULL and
+// ckpt_every == 0 for none; the caller has checked ckpt_every).
+gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, const void* v,
+                        const float* log_g, const float* beta, const float* h0, float* hT,
+                        void* o, float* h_ckpt, int ckpt_every, void* workspace,
+                        size_t workspace_bytes, void* hip_stream) {
     const size_t es = dsize(p);
     const size_t BT = (size_t)p->B * p->T;
     const size_t qk_bytes = BT * p->Hk * p->dk * es;
     const size_t v_bytes = BT * p->Hv * p->dv * es;
     const size_t g_bytes = BT * p->Hv * sizeof(float);
     const size_t s_bytes = (size_t)p->B * p->Hv * p->dk * p->dv * sizeof(float);
+    const int nck = ckpt_every > 0 ? (p->T + ckpt_every - 1) / ckpt_every : 0;
+    const size_t ck_bytes = s_bytes * (size_t)nck;
 
     if (BT > 0 && (!q || !k || !v || !log_g || !beta || !o)) return GDN_ERR_NULL_POINTER;
-    const void* ptrs[] = {q, k, v, log_g, beta, h0, hT, o, workspace};
+    if (ck_bytes > 0 && !h_ckpt) return GDN_ERR_NULL_POINTER;
+    const void* ptrs[] = {q, k, v, log_g, beta, h0, hT, o, workspace, h_ckpt};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
 
@@ -132,12 +140,16 @@ gdn_status gdn_chunk_prefill(const gdn_problem* p, const void* q, const void* k,
     const Range r_hT = range_of(hT, hT ? s_bytes : 0);
     const Range r_h0 = range_of(h0, h0 ? s_bytes : 0);
     const Range r_ws = range_of(workspace, workspace ? need_ws : 0);
+    const Range r_ck = range_of(h_ckpt, h_ckpt ? ck_bytes : 0);
     for (const Range& in : ins) {
-        if (overlaps(in, r_o) || overlaps(in, r_hT) || overlaps(in, r_ws)) return GDN_ERR_ALIAS;
+        if (overlaps(in, r_o) || overlaps(in, r_hT) || overlaps(in, r_ws) || overlaps(in, r_ck))
+            return GDN_ERR_ALIAS;
     }
     if (overlaps(r_o, r_hT) || overlaps(r_o, r_h0) || overlaps(r_o, r_ws)) return GDN_ERR_ALIAS;
     if (overlaps(r_hT, r_ws) || overlaps(r_h0, r_ws)) return GDN_ERR_ALIAS;
     if (hT && h0 && hT != h0 && overlaps(r_hT, r_h0)) return GDN_ERR_ALIAS;
+    if (overlaps(r_ck, r_o) || overlaps(r_ck, r_hT) || overlaps(r_ck, r_h0) || overlaps(r_ck, r_ws))
+        return GDN_ERR_ALIAS;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (p->B == 0 || p->Hv == 0) return GDN_OK;
@@ -149,8 +161,37 @@ gdn_status gdn_chunk_prefill(const gdn_problem* p, const void* q, const void* k,
     gdn::PrefillArgs a = prefill_args(p);
     a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
     a.h0 = h0; a.hT = hT; a.o = o; a.ws = workspace; a.ws_bytes = workspace_bytes;
+    a.ckpt = nck > 0 ? h_ckpt : nullptr;
+    a.ckpt_every = nck > 0 ? ckpt_every : 0;
+    a.nck = nck;
     err = use_mfma(a) ? gdn::launch_prefill_mfma(a, stream) : gdn::launch_prefill_generic(a, stream);
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_prefill(const gdn_problem* p, const void* q, const void* k, const void* v,
+                             const float* log_g, const float* beta, const float* h0, float* hT,
+                             void* o, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const gdn_status st = check_problem(p, false);
+    if (st != GDN_OK) return st;
+    return prefill_impl(p, q, k, v, log_g, beta, h0, hT, o, nullptr, 0, workspace,
+                        workspace_bytes, hip_stream);
+}
+
+gdn_status gdn_chunk_prefill_ckpt(const gdn_problem* p, const void* q, const void* k,
+                                  const void* v, const float* log_g, const float* beta,
+                                  const float* h0, float* hT, void* o, float* h_ckpt,
+                                  int32_t ckpt_every, void* workspace, size_t workspace_bytes,
+                                  void* hip_stream) {
+    const gdn_status st = check_problem(p, false);
+    if (st != GDN_OK) return st;
+    const int C = p->chunk ? p->chunk : 64;
+    if (ckpt_every <= 0 || ckpt_every % C != 0) return GDN_ERR_BAD_SHAPE;
+    return prefill_impl(p, q, k, v, log_g, beta, h0, hT, o, h_ckpt, ckpt_every, workspace,
+                        workspace_bytes, hip_stream);
 }
 
 gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, const void* v,

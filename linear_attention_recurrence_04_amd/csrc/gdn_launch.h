@@ -30,6 +30,9 @@ struct PrefillArgs {
     void* o;
     void* ws;          // workspace (validated size)
     size_t ws_bytes;
+    float* ckpt;       // [B, nck, Hv, D, D] state checkpoints, or null
+    int ckpt_every;    // tokens between checkpoints (a multiple of C), 0 if none
+    int nck;           // ceil(T / ckpt_every), 0 if none
 };
 
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);

@@ -23,7 +23,8 @@
 // Mapping: one workgroup per (b, value head, 32-column block of the state);
 // columns of the state evolve independently, so the blocks never communicate.
 // Everything of a chunk lives in LDS; the state block stays in LDS across all
-// chunks and touches HBM only at the start (h0) and the end (hT).
+// chunks and touches HBM only at the start (h0), the end (hT) and at the
+// optional checkpoints.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -34,7 +35,8 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ log_g, const float* __restrict__ beta,
     const float* h0, float* hT, TIn* __restrict__ o,
-    int T, int Hk, int Hv, int l2norm, float q_scale) {
+    int T, int Hk, int Hv, int l2norm, float q_scale,
+    float* __restrict__ ckpt, int ckpt_every, int nck) {
     constexpr int NT = 256;
     constexpr int TPR = NT / C;   // threads per chunk row (normalisation)
     constexpr int P = NT / BV;    // partial-sum lanes per column (solve)
@@ -167,13 +169,19 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(
             }
         }
         __syncthreads();
-        // state hand-off
+        // state hand-off; a checkpoint slot receives the state after every
+        // ckpt_every tokens and after the last token
         const float GL = Gm[C - 1];
+        const int done = t0 + L;
+        float* ck = nullptr;
+        if (ckpt && (done % ckpt_every == 0 || done == T))
+            ck = ckpt + (((size_t)b * nck + (done + ckpt_every - 1) / ckpt_every - 1) * Hv + h) * D * D;
         for (int e = tid; e < D * BV; e += NT) {
             const int i = e / BV, j = e % BV;
             float acc = GL * Ss[i][j];
             for (int s = 0; s < L; ++s) acc += Wd[s] * Ks[s][i] * Xs[s][j];
             Ss[i][j] = acc;
+            if (ck) ck[(size_t)i * D + j0 + j] = acc;
         }
     }
     __syncthreads();
@@ -192,7 +200,8 @@ static hipError_t launch_generic(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_generic_kernel<D, C, BV, TIn>), grid, dim3(256), 0, stream,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.v), a.log_g, a.beta, a.h0, a.hT,
-                       static_cast<TIn*>(a.o), a.T, a.Hk, a.Hv, a.l2norm, a.q_scale);
+                       static_cast<TIn*>(a.o), a.T, a.Hk, a.Hv, a.l2norm, a.q_scale,
+                       a.ckpt, a.ckpt_every, a.nck);
     return hipGetLastError();
 }
 

@@ -524,7 +524,8 @@ __device__ __forceinline__ s16x4 ld_tr4(const void* p) {
 __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const unsigned char* __restrict__ ws, const float* h0, float* hT, bf16_t* __restrict__ o,
-    int T, int NTc, int Hk, int Hv, float q_scale, int xcd_remap) {
+    int T, int NTc, int Hk, int Hv, float q_scale, int xcd_remap,
+    float* __restrict__ ckpt, int ckpt_every, int nck) {
     __shared__ ScanSmem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -820,6 +821,19 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 for (int a = 0; a < 8; ++a) S[a] = mfma32(akt[a][0], DWB0, S[a] * GC);
 #pragma unroll
                 for (int a = 0; a < 8; ++a) S[a] = mfma32(akt[a][1], DWB1, S[a]);
+                // ---- checkpoint slot: the state after every ckpt_every tokens
+                //      and after the last token
+                if (ckpt) {
+                    const int done = min((c + 1) * C, T);
+                    if (done % ckpt_every == 0 || c == NTc - 1) {
+                        const int slot = (done + ckpt_every - 1) / ckpt_every - 1;
+                        float* cp = ckpt + (((size_t)b * nck + slot) * Hv + h) * D * D + jw + n;
+#pragma unroll
+                        for (int a = 0; a < 8; ++a)
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) cp[(32 * (a >> 1) + 8 * g + 4 * (a & 1) + t) * D] = S[a][t];
+                    }
+                }
             }
             __syncthreads();
         }
@@ -933,7 +947,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(chunk_scan_kernel, dim3(scan_blocks), dim3(SNT), 0, stream,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
                        static_cast<const bf16_t*>(a.v), ws, a.h0, a.hT,
-                       static_cast<bf16_t*>(a.o), a.T, NTc, a.Hk, a.Hv, a.q_scale, remap);
+                       static_cast<bf16_t*>(a.o), a.T, NTc, a.Hk, a.Hv, a.q_scale, remap,
+                       a.ckpt, a.ckpt_every, a.nck);
     return hipGetLastError();
 }
 

@@ -105,3 +105,26 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError):
         B.gdn_chunk_prefill(x, x, x, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1))
+
+
+def prefill_ckpt(prob, every, ck=fake(8), q=fake(0), k=fake(1), v=fake(2), lg=fake(3),
+                 bt=fake(4), h0=None, hT=fake(6), o=fake(7)):
+    return B.lib().gdn_chunk_prefill_ckpt(ctypes.byref(prob), q, k, v, lg, bt, h0, hT, o, ck,
+                                          every, None, 0, None)
+
+
+def test_checkpointed_prefill_rejects_bad_arguments():
+    # ckpt_every must be a positive multiple of the chunk in use (chunk 0 means 64)
+    assert prefill_ckpt(P(), 0) == 2
+    assert prefill_ckpt(P(), -32) == 2
+    assert prefill_ckpt(P(), 48) == 2                  # chunk 32
+    assert prefill_ckpt(P(chunk=0), 32) == 2           # chunk 64
+    assert prefill_ckpt(P(Hv=3), 64) == 2              # the problem is checked first
+    assert prefill_ckpt(P(), 64, ck=None) == 1         # T > 0 needs the slots
+    assert prefill_ckpt(P(), 64, ck=fake(8, 4)) == 4
+    assert prefill_ckpt(P(), 64, ck=fake(7, 512)) == 7      # slots inside o
+    assert prefill_ckpt(P(), 64, ck=fake(6, 0)) == 7        # slots over hT
+    assert prefill_ckpt(P(), 32, ck=fake(0, 4096)) == 7     # slots inside q
+    # 4 slots of 1*2*64*64 fp32 = 131072 bytes: one byte short of hT's start
+    # still overlaps; the call is then rejected before any launch
+    assert prefill_ckpt(P(), 32, ck=fake(6, -131072 + 16)) == 7
