@@ -7,7 +7,8 @@ half of the metric (B=64 sequences, same heads, one token per step for 1000
 steps, fp32 state updated in place) is timed in the same run and reported
 under "decode" as state-update HBM GB/s and tokens/s.  The same prefill call
 storing a state checkpoint every 512 tokens (gdn_chunk_prefill_ckpt) is timed
-too and reported under "checkpoints".
+too and reported under "checkpoints", and the call that forms the gates from
+raw projections (gdn_chunk_prefill_gated) under "raw_gates".
 
 Inputs are seeded synthetic tensors already resident in HBM when the timed
 region starts.  Kernel time comes from HIP events recorded on the stream the
@@ -116,9 +117,10 @@ def time_stream(torch, fn, steps: int):
     return start.elapsed_time(stop)  # ms
 
 
-def bench_prefill(torch, gdn, p, steps, warmup, ckpt_every: int = 0):
+def bench_prefill(torch, gdn, p, steps, warmup, ckpt_every: int = 0, raw_gates: bool = False):
     """ms per prefill call; with ckpt_every > 0 the call also stores the state
-    every ckpt_every tokens (gdn_chunk_prefill_ckpt)."""
+    every ckpt_every tokens (gdn_chunk_prefill_ckpt); with raw_gates the gates
+    are formed in the kernels from raw projections (gdn_chunk_prefill_gated)."""
     log(f"prefill workload {p.name}: generating inputs")
     inp = gi.make_prefill(p, 0)
     dev = {n: torch.from_numpy(inp[n]).cuda() for n in ("q", "k", "v", "log_g", "beta", "h0")}
@@ -131,7 +133,14 @@ def bench_prefill(torch, gdn, p, steps, warmup, ckpt_every: int = 0):
     ws_bytes = gdn.gdn_chunk_prefill_workspace_bytes(prob)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
-    if ckpt_every:
+    if raw_gates:
+        rg = {n: torch.from_numpy(x).cuda() for n, x in gi.make_raw_gates((p.B, p.T), p.Hv, 0).items()}
+
+        def call():
+            gdn.gdn_chunk_prefill_gated(dev["q"], dev["k"], dev["v"], rg["a"], rg["b"], rg["A_log"],
+                                        rg["dt_bias"], dev["h0"], chunk=p.chunk, out=out, hT=hT,
+                                        workspace=ws)
+    elif ckpt_every:
         nck = -(-p.T // ckpt_every)
         ck = torch.empty((p.B, nck, p.Hv, p.dk, p.dv), dtype=torch.float32, device="cuda")
 
@@ -147,8 +156,8 @@ def bench_prefill(torch, gdn, p, steps, warmup, ckpt_every: int = 0):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    log(f"prefill{' with checkpoints every %d' % ckpt_every if ckpt_every else ''}: "
-        f"timing {steps} steps")
+    log(f"prefill{' with checkpoints every %d' % ckpt_every if ckpt_every else ''}"
+        f"{' with raw gates' if raw_gates else ''}: timing {steps} steps")
     ms = time_stream(torch, call, steps)
     return ms / steps, prob
 
@@ -286,6 +295,14 @@ def main():
                                                if ms_c > ms else None),
         }
         log(f"prefill with {nck} checkpoints: {ms_c:.3f} ms/call ({(ms_c - ms) * 1e3:+.1f} us)")
+        # the same call forming log g and beta in the kernels from raw projections
+        ms_g, _ = bench_prefill(torch, gdn, p, args.steps, args.warmup, raw_gates=True)
+        result["raw_gates"] = {
+            "ms_per_call": round(ms_g, 4), "delta_ms_vs_precomputed_gates": round(ms_g - ms, 4),
+            "tokens_per_s": round(p.B * p.T / (ms_g * 1e-3), 1),
+            "gate_tensor_bytes_not_materialised": 2 * p.B * p.T * p.Hv * 4 * 2,
+        }
+        log(f"prefill with raw gates: {ms_g:.3f} ms/call ({(ms_g - ms) * 1e3:+.1f} us)")
 
     if args.only in ("all", "decode"):
         ms_d = bench_decode(torch, gdn, d, args.decode_steps, min(args.warmup, 10) or 1)

@@ -177,6 +177,44 @@ gdn_status gdn_decode_step(const gdn_problem* problem,
                            float* state, void* o, void* hip_stream);
 
 /*
+ * Fused gate prologue.  The two variants below take the gate projections of
+ * the model instead of log g and beta, and form the gates inside the kernels:
+ *
+ *     log g = -exp(A_log[h]) * softplus(a + dt_bias[h]),   beta = sigmoid(b)
+ *
+ * ("Qwen3.5 Gated Delta Net NKI Kernel for AWS Neuron", section "Correctness
+ * Contract", gives this decay law of the Hugging Face Qwen3.5 layer.  The
+ * pages do not spell out beta; the logistic of its projection is taken, the
+ * plain way to a write strength in (0, 1)).  log g is never positive, so the
+ * state never grows.
+ * softplus(x) = log(1 + e^x).  This saves writing and reading log g and beta
+ * as separate [B, T, Hv] tensors.
+ *
+ *   a, b           same shapes and dtype as log_g, beta (fp32 [B, T, Hv]
+ *                  for prefill, [B, Hv] for decode): the raw projections
+ *   A_log, dt_bias [Hv] fp32 per-value-head gate parameters
+ *
+ * gdn_chunk_prefill_gated: every other argument as gdn_chunk_prefill_ckpt
+ * (h_ckpt may be NULL with ckpt_every == 0 for no checkpoints).
+ * gdn_decode_step_gated: every other argument as gdn_decode_step.
+ * The results equal those of the plain entry points called with the log g and
+ * beta above computed in fp32.
+ */
+gdn_status gdn_chunk_prefill_gated(const gdn_problem* problem,
+                                   const void* q, const void* k, const void* v,
+                                   const float* a, const float* b,
+                                   const float* A_log, const float* dt_bias,
+                                   const float* h0, float* hT, void* o,
+                                   float* h_ckpt, int32_t ckpt_every,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* hip_stream);
+gdn_status gdn_decode_step_gated(const gdn_problem* problem,
+                                 const void* q, const void* k, const void* v,
+                                 const float* a, const float* b,
+                                 const float* A_log, const float* dt_bias,
+                                 float* state, void* o, void* hip_stream);
+
+/*
  * Name of the prefill kernel variant gdn_chunk_prefill launches for this
  * problem (static storage, never NULL): "generic_f32" (fp32 arithmetic, any
  * supported shape), "mfma_bf16" (bf16 MFMA path for bf16 inputs, d = 128,

@@ -63,6 +63,11 @@ def lib():
     L.gdn_chunk_prefill_ckpt.restype = ctypes.c_int
     L.gdn_chunk_prefill_ckpt.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, vp, fp, ctypes.c_int32,
                                          vp, sz, vp]
+    L.gdn_chunk_prefill_gated.restype = ctypes.c_int
+    L.gdn_chunk_prefill_gated.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp, fp,
+                                          ctypes.c_int32, vp, sz, vp]
+    L.gdn_decode_step_gated.restype = ctypes.c_int
+    L.gdn_decode_step_gated.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
     L.gdn_decode_step.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [pp, vp, vp, vp, fp, fp, fp, vp, vp]
     _lib = L
@@ -260,5 +265,85 @@ def gdn_decode_step(q, k, v, log_g, beta, state, *, qk_l2norm: bool = True,
                         q_scale=q_scale)
     st = lib().gdn_decode_step(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g),
                                _ptr(beta), _ptr(state), _ptr(out), _stream(stream))
+    _check(st)
+    return out
+
+
+def gdn_chunk_prefill_gated(q, k, v, a, b, A_log, dt_bias, h0=None, *, ckpt_every: int = 0,
+                            chunk: int = 64, qk_l2norm: bool = True, q_scale: float = 1.0,
+                            out=None, hT=None, h_ckpt=None, workspace=None, stream=None):
+    """Chunked prefill with the gates formed in the kernels from the raw
+    projections a, b [B,T,Hv] fp32 and per-head A_log, dt_bias [Hv] fp32:
+    log g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b).
+    Returns (o, hT, h_ckpt); h_ckpt is None unless ckpt_every > 0."""
+    torch = _torch()
+    _need(q, "q")
+    dt = _dtype_code(q)
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    _need(k, "k", q.dtype, q.shape)
+    _need(v, "v", q.dtype, (B, T, Hv, dv))
+    _need(a, "a", torch.float32, (B, T, Hv))
+    _need(b, "b", torch.float32, (B, T, Hv))
+    _need(A_log, "A_log", torch.float32, (Hv,))
+    _need(dt_bias, "dt_bias", torch.float32, (Hv,))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, Hv, dk, dv))
+    every = int(ckpt_every)
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(out, "out", q.dtype, (B, T, Hv, dv))
+    if hT is None:
+        hT = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=q.device)
+    else:
+        _need(hT, "hT", torch.float32, (B, Hv, dk, dv))
+    ck_ptr = None
+    if every > 0:
+        nck = -(-T // every)
+        if h_ckpt is None:
+            h_ckpt = torch.empty((B, nck, Hv, dk, dv), dtype=torch.float32, device=q.device)
+        else:
+            _need(h_ckpt, "h_ckpt", torch.float32, (B, nck, Hv, dk, dv))
+        ck_ptr = _ptr(h_ckpt) if h_ckpt.numel() else None
+    prob = make_problem(B, T, Hk, Hv, dk, dv, chunk=chunk, dtype=dt, qk_l2norm=qk_l2norm,
+                        q_scale=q_scale)
+    need = gdn_chunk_prefill_workspace_bytes(prob)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().gdn_chunk_prefill_gated(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                       _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(h0), _ptr(hT),
+                                       _ptr(out), ck_ptr, every, _ptr(workspace), ws_bytes,
+                                       _stream(stream))
+    _check(st)
+    return out, hT, (h_ckpt if every > 0 else None)
+
+
+def gdn_decode_step_gated(q, k, v, a, b, A_log, dt_bias, state, *, qk_l2norm: bool = True,
+                          q_scale: float = 1.0, out=None, stream=None):
+    """One decode step with the gates formed in the kernel from a, b [B,Hv] fp32
+    and A_log, dt_bias [Hv] fp32; state [B,Hv,d,d] is updated in place."""
+    torch = _torch()
+    _need(q, "q")
+    dt = _dtype_code(q)
+    B, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    _need(k, "k", q.dtype, q.shape)
+    _need(v, "v", q.dtype, (B, Hv, dv))
+    _need(a, "a", torch.float32, (B, Hv))
+    _need(b, "b", torch.float32, (B, Hv))
+    _need(A_log, "A_log", torch.float32, (Hv,))
+    _need(dt_bias, "dt_bias", torch.float32, (Hv,))
+    _need(state, "state", torch.float32, (B, Hv, dk, dv))
+    if out is None:
+        out = torch.empty((B, Hv, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(out, "out", q.dtype, (B, Hv, dv))
+    prob = make_problem(B, 1, Hk, Hv, dk, dv, chunk=0, dtype=dt, qk_l2norm=qk_l2norm,
+                        q_scale=q_scale)
+    st = lib().gdn_decode_step_gated(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                     _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(state), _ptr(out),
+                                     _stream(stream))
     _check(st)
     return out

@@ -25,6 +25,7 @@ template <int D, typename TIn>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ log_g, const float* __restrict__ beta,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     float* __restrict__ state, TIn* __restrict__ o,
     int Hk, int Hv, int l2norm, float q_scale) {
     constexpr int NT = 256;
@@ -107,8 +108,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     __syncthreads();
 
     // 4. column totals, delta and the output (one thread per column)
-    const float g = expf(log_g[bh]);
-    const float bt = beta[bh];
+    float lgv = log_g[bh], bt = beta[bh];
+    if (A_log) {   // raw projections a, b
+        const int h = bh % Hv;
+        lgv = raw_log_decay(lgv, A_log[h], dt_bias[h]);
+        bt = raw_beta(bt);
+    }
+    const float g = expf(lgv);
     if (tid < D) {
         float a = 0.f, c = 0.f;
 #pragma unroll
@@ -146,7 +152,7 @@ static hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL((decode_step_kernel<D, TIn>), dim3(blocks), dim3(256), 0, stream,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                       static_cast<const TIn*>(a.v), a.log_g, a.beta, a.state,
+                       static_cast<const TIn*>(a.v), a.log_g, a.beta, a.A_log, a.dt_bias, a.state,
                        static_cast<TIn*>(a.o), a.Hk, a.Hv, a.l2norm, a.q_scale);
     return hipGetLastError();
 }

@@ -109,10 +109,12 @@ size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* p) {
 namespace {
 
 // gdn_chunk_prefill with optional checkpoints (h_ckpt == NULL and
-// ckpt_every == 0 for none; the caller has checked ckpt_every).
+// ckpt_every == 0 for none; the caller has checked ckpt_every) and optional
+// raw gates (A_log, dt_bias non-null: log_g, beta hold the projections a, b).
 gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, const void* v,
-                        const float* log_g, const float* beta, const float* h0, float* hT,
-                        void* o, float* h_ckpt, int ckpt_every, void* workspace,
+                        const float* log_g, const float* beta, const float* A_log,
+                        const float* dt_bias, const float* h0, float* hT, void* o,
+                        float* h_ckpt, int ckpt_every, void* workspace,
                         size_t workspace_bytes, void* hip_stream) {
     const size_t es = dsize(p);
     const size_t BT = (size_t)p->B * p->T;
@@ -125,7 +127,7 @@ gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, cons
 
     if (BT > 0 && (!q || !k || !v || !log_g || !beta || !o)) return GDN_ERR_NULL_POINTER;
     if (ck_bytes > 0 && !h_ckpt) return GDN_ERR_NULL_POINTER;
-    const void* ptrs[] = {q, k, v, log_g, beta, h0, hT, o, workspace, h_ckpt};
+    const void* ptrs[] = {q, k, v, log_g, beta, h0, hT, o, workspace, h_ckpt, A_log, dt_bias};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
 
@@ -133,9 +135,11 @@ gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, cons
     if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return GDN_ERR_WORKSPACE;
 
     // outputs against inputs: hT may be exactly h0, nothing else may overlap
+    const size_t par_bytes = (size_t)p->Hv * sizeof(float);
     const Range ins[] = {range_of(q, BT ? qk_bytes : 0), range_of(k, BT ? qk_bytes : 0),
                          range_of(v, BT ? v_bytes : 0), range_of(log_g, BT ? g_bytes : 0),
-                         range_of(beta, BT ? g_bytes : 0)};
+                         range_of(beta, BT ? g_bytes : 0), range_of(A_log, A_log ? par_bytes : 0),
+                         range_of(dt_bias, dt_bias ? par_bytes : 0)};
     const Range r_o = range_of(o, BT ? v_bytes : 0);
     const Range r_hT = range_of(hT, hT ? s_bytes : 0);
     const Range r_h0 = range_of(h0, h0 ? s_bytes : 0);
@@ -160,6 +164,7 @@ gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, cons
     }
     gdn::PrefillArgs a = prefill_args(p);
     a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
+    a.A_log = A_log; a.dt_bias = dt_bias;
     a.h0 = h0; a.hT = hT; a.o = o; a.ws = workspace; a.ws_bytes = workspace_bytes;
     a.ckpt = nck > 0 ? h_ckpt : nullptr;
     a.ckpt_every = nck > 0 ? ckpt_every : 0;
@@ -177,8 +182,8 @@ gdn_status gdn_chunk_prefill(const gdn_problem* p, const void* q, const void* k,
                              void* o, void* workspace, size_t workspace_bytes, void* hip_stream) {
     const gdn_status st = check_problem(p, false);
     if (st != GDN_OK) return st;
-    return prefill_impl(p, q, k, v, log_g, beta, h0, hT, o, nullptr, 0, workspace,
-                        workspace_bytes, hip_stream);
+    return prefill_impl(p, q, k, v, log_g, beta, nullptr, nullptr, h0, hT, o, nullptr, 0,
+                        workspace, workspace_bytes, hip_stream);
 }
 
 gdn_status gdn_chunk_prefill_ckpt(const gdn_problem* p, const void* q, const void* k,
@@ -190,27 +195,46 @@ gdn_status gdn_chunk_prefill_ckpt(const gdn_problem* p, const void* q, const voi
     if (st != GDN_OK) return st;
     const int C = p->chunk ? p->chunk : 64;
     if (ckpt_every <= 0 || ckpt_every % C != 0) return GDN_ERR_BAD_SHAPE;
-    return prefill_impl(p, q, k, v, log_g, beta, h0, hT, o, h_ckpt, ckpt_every, workspace,
-                        workspace_bytes, hip_stream);
+    return prefill_impl(p, q, k, v, log_g, beta, nullptr, nullptr, h0, hT, o, h_ckpt,
+                        ckpt_every, workspace, workspace_bytes, hip_stream);
 }
 
-gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, const void* v,
-                           const float* log_g, const float* beta, float* state, void* o,
-                           void* hip_stream) {
-    gdn_status st = check_problem(p, true);
+gdn_status gdn_chunk_prefill_gated(const gdn_problem* p, const void* q, const void* k,
+                                   const void* v, const float* a, const float* b,
+                                   const float* A_log, const float* dt_bias, const float* h0,
+                                   float* hT, void* o, float* h_ckpt, int32_t ckpt_every,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const gdn_status st = check_problem(p, false);
     if (st != GDN_OK) return st;
+    if (!A_log || !dt_bias) return GDN_ERR_NULL_POINTER;
+    const int C = p->chunk ? p->chunk : 64;
+    if (ckpt_every < 0 || ckpt_every % C != 0) return GDN_ERR_BAD_SHAPE;
+    if (ckpt_every == 0 && h_ckpt) return GDN_ERR_BAD_SHAPE;
+    return prefill_impl(p, q, k, v, a, b, A_log, dt_bias, h0, hT, o, h_ckpt, ckpt_every,
+                        workspace, workspace_bytes, hip_stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+gdn_status decode_impl(const gdn_problem* p, const void* q, const void* k, const void* v,
+                       const float* log_g, const float* beta, const float* A_log,
+                       const float* dt_bias, float* state, void* o, void* hip_stream) {
     if (p->B > 0 && (!q || !k || !v || !log_g || !beta || !state || !o))
         return GDN_ERR_NULL_POINTER;
-    const void* ptrs[] = {q, k, v, log_g, beta, state, o};
+    const void* ptrs[] = {q, k, v, log_g, beta, state, o, A_log, dt_bias};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
     const size_t es = dsize(p);
     const size_t B = (size_t)p->B;
+    const size_t par_bytes = (size_t)p->Hv * sizeof(float);
     const Range r_state = range_of(state, B * p->Hv * p->dk * p->dv * sizeof(float));
     const Range r_o = range_of(o, B * p->Hv * p->dv * es);
     const Range ins[] = {range_of(q, B * p->Hk * p->dk * es), range_of(k, B * p->Hk * p->dk * es),
                          range_of(v, B * p->Hv * p->dv * es), range_of(log_g, B * p->Hv * 4),
-                         range_of(beta, B * p->Hv * 4)};
+                         range_of(beta, B * p->Hv * 4), range_of(A_log, A_log ? par_bytes : 0),
+                         range_of(dt_bias, dt_bias ? par_bytes : 0)};
     for (const Range& in : ins)
         if (overlaps(in, r_state) || overlaps(in, r_o)) return GDN_ERR_ALIAS;
     if (overlaps(r_state, r_o)) return GDN_ERR_ALIAS;
@@ -221,9 +245,33 @@ gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, c
     a.bf16 = p->dtype == GDN_DTYPE_BF16;
     a.l2norm = p->qk_l2norm;
     a.q_scale = p->q_scale;
-    a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta; a.state = state; a.o = o;
+    a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
+    a.A_log = A_log; a.dt_bias = dt_bias;
+    a.state = state; a.o = o;
     const hipError_t err = gdn::launch_decode_step(a, static_cast<hipStream_t>(hip_stream));
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, const void* v,
+                           const float* log_g, const float* beta, float* state, void* o,
+                           void* hip_stream) {
+    const gdn_status st = check_problem(p, true);
+    if (st != GDN_OK) return st;
+    return decode_impl(p, q, k, v, log_g, beta, nullptr, nullptr, state, o, hip_stream);
+}
+
+gdn_status gdn_decode_step_gated(const gdn_problem* p, const void* q, const void* k,
+                                 const void* v, const float* a, const float* b,
+                                 const float* A_log, const float* dt_bias, float* state,
+                                 void* o, void* hip_stream) {
+    const gdn_status st = check_problem(p, true);
+    if (st != GDN_OK) return st;
+    if (!A_log || !dt_bias) return GDN_ERR_NULL_POINTER;
+    return decode_impl(p, q, k, v, a, b, A_log, dt_bias, state, o, hip_stream);
 }
 
 }  // extern "C"

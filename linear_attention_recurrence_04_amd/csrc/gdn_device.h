@@ -35,6 +35,17 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Qwen gates from the raw per-token projections a, b of a value head with
+// parameters A_log, dt_bias: log g = -exp(A_log) softplus(a + dt_bias) (never
+// positive) and beta = sigmoid(b).  softplus(x) = log(1 + e^x), taken as x
+// itself above 20 where the two agree in fp32.
+__device__ __forceinline__ float raw_log_decay(float a, float A_log, float dt_bias) {
+    const float x = a + dt_bias;
+    const float sp = x > 20.f ? x : log1pf(expf(x));
+    return -expf(A_log) * sp;
+}
+__device__ __forceinline__ float raw_beta(float b) { return 1.0f / (1.0f + expf(-b)); }
+
 // 1 / max(sqrt(ss), 1e-6): the L2-normalisation factor used by every kernel.
 __device__ __forceinline__ float inv_l2(float ss) {
     return 1.0f / fmaxf(sqrtf(ss), 1e-6f);

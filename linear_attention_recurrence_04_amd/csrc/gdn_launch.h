@@ -13,7 +13,8 @@ struct DecodeArgs {
     int l2norm;
     float q_scale;
     const void *q, *k, *v;
-    const float *log_g, *beta;
+    const float *log_g, *beta;   // or the raw projections a, b when A_log is set
+    const float *A_log, *dt_bias;  // [Hv] gate parameters, or null
     float* state;
     void* o;
 };
@@ -24,7 +25,8 @@ struct PrefillArgs {
     int l2norm;
     float q_scale;
     const void *q, *k, *v;
-    const float *log_g, *beta;
+    const float *log_g, *beta;   // or the raw projections a, b when A_log is set
+    const float *A_log, *dt_bias;  // [Hv] gate parameters, or null
     const float* h0;   // may be null (zeros)
     float* hT;         // may be null; may equal h0
     void* o;

@@ -34,6 +34,7 @@ template <int D, int C, int BV, typename TIn>
 __global__ __launch_bounds__(256) void prefill_generic_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ log_g, const float* __restrict__ beta,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     const float* h0, float* hT, TIn* __restrict__ o,
     int T, int Hk, int Hv, int l2norm, float q_scale,
     float* __restrict__ ckpt, int ckpt_every, int nck) {
@@ -84,8 +85,13 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(
         if (tid < C) {
             const bool in = tid < L;
             const size_t gi = ((size_t)b * T + t0 + tid) * Hv + h;
-            lgs[tid] = in ? log_g[gi] : 0.f;   // padding rows: g = 1, beta = 0, k = q = 0
-            bts[tid] = in ? beta[gi] : 0.f;
+            float lgv = in ? log_g[gi] : 0.f, btv = in ? beta[gi] : 0.f;
+            if (A_log && in) {   // raw projections a, b
+                lgv = raw_log_decay(lgv, A_log[h], dt_bias[h]);
+                btv = raw_beta(btv);
+            }
+            lgs[tid] = lgv;   // padding rows: g = 1, beta = 0, k = q = 0
+            bts[tid] = btv;
         }
         __syncthreads();
 
@@ -199,7 +205,7 @@ static hipError_t launch_generic(const PrefillArgs& a, hipStream_t stream) {
     dim3 grid(a.B * a.Hv, D / BV);
     hipLaunchKernelGGL((prefill_generic_kernel<D, C, BV, TIn>), grid, dim3(256), 0, stream,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                       static_cast<const TIn*>(a.v), a.log_g, a.beta, a.h0, a.hT,
+                       static_cast<const TIn*>(a.v), a.log_g, a.beta, a.A_log, a.dt_bias, a.h0, a.hT,
                        static_cast<TIn*>(a.o), a.T, a.Hk, a.Hv, a.l2norm, a.q_scale,
                        a.ckpt, a.ckpt_every, a.nck);
     return hipGetLastError();

@@ -245,6 +245,7 @@ __device__ __forceinline__ void gate_tiles(PrepSmem& sm, const f32x4 (&gram)[5],
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const float* __restrict__ log_g, const float* __restrict__ beta,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     unsigned char* __restrict__ ws, int T, int NTc, int Hk, int Hv, int l2norm) {
     __shared__ PrepSmem sm;
     const int tid = threadIdx.x;
@@ -268,6 +269,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ch
         const size_t gi = ((size_t)b * T + t0 + min(lane, L - 1)) * Hv + hk * rr + j;
         lgr = log_g[gi];
         btr = beta[gi];
+        if (A_log) {   // raw projections a, b
+            lgr = raw_log_decay(lgr, A_log[hk * rr + j], dt_bias[hk * rr + j]);
+            btr = raw_beta(btr);
+        }
     };
     float lg_next, bt_next;
     gate_in(0, lg_next, bt_next);
@@ -939,7 +944,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
     unsigned char* ws = static_cast<unsigned char*>(a.ws);
     hipLaunchKernelGGL(chunk_prep_kernel, dim3(prep_blocks), dim3(NT), 0, stream,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k), a.log_g, a.beta,
-                       ws, a.T, NTc, a.Hk, a.Hv, a.l2norm);
+                       a.A_log, a.dt_bias, ws, a.T, NTc, a.Hk, a.Hv, a.l2norm);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int scan_blocks = a.B * a.Hv * (D / BVS);

@@ -222,3 +222,16 @@ def custom_prefill(B: int, T: int, Hk: int, Hv: int, dk: int, dv: int, *, seed: 
     """Same recipe at an arbitrary shape (edge cases and sweeps)."""
     p = Problem("custom", B, T, Hk, Hv, dk, dv, chunk, dtype, gate, h0, gate_lo, gate_hi)
     return make_prefill(p, seed)
+
+
+def make_raw_gates(shape_rows: tuple, Hv: int, seed: int) -> dict:
+    """Raw gate inputs of the fused gate prologue, fp32: projections a, b
+    [*shape_rows, Hv] ~ N(0, 1); per-value-head A_log ~ U(-2, 1) and
+    dt_bias ~ N(0, 0.5^2).  (The gate law itself is applied by the kernels
+    and by the oracle, not here.)"""
+    rng = np.random.default_rng(10_000 + seed)
+    a = rng.standard_normal(tuple(shape_rows) + (Hv,)).astype(np.float32)
+    b = rng.standard_normal(tuple(shape_rows) + (Hv,)).astype(np.float32)
+    A_log = rng.uniform(-2.0, 1.0, Hv).astype(np.float32)
+    dt_bias = (0.5 * rng.standard_normal(Hv)).astype(np.float32)
+    return {"a": a, "b": b, "A_log": A_log, "dt_bias": dt_bias}

@@ -56,6 +56,8 @@ def _declare(lib):
     lib.oracle_unit_lower_inverse.argtypes = [i, dp, dp]
     lib.oracle_neumann_inverse.restype = i
     lib.oracle_neumann_inverse.argtypes = [i, dp, dp]
+    lib.oracle_qwen_gates.restype = i
+    lib.oracle_qwen_gates.argtypes = [ctypes.c_long, i, dp, dp, dp, dp, dp, dp]
     return lib
 
 
@@ -153,3 +155,21 @@ def neumann_inverse(A, lib=None) -> np.ndarray:
     if lib.oracle_neumann_inverse(n, _ptr(A), _ptr(out)) != 0:
         raise ValueError("oracle_neumann_inverse failed")
     return out
+
+
+def qwen_gates(a, b, A_log, dt_bias, lib=None) -> Tuple[np.ndarray, np.ndarray]:
+    """(log_g, beta) from raw projections a, b [..., Hv] and per-head A_log,
+    dt_bias [Hv]: log g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b)."""
+    lib = lib or load()
+    a, b, A_log, dt_bias = map(_f64, (a, b, A_log, dt_bias))
+    Hv = A_log.shape[0]
+    if a.shape != b.shape or a.shape[-1] != Hv or dt_bias.shape != (Hv,):
+        raise ValueError("inconsistent gate shapes")
+    n = a.size // Hv
+    log_g = np.zeros(a.shape)
+    beta = np.zeros(a.shape)
+    rc = lib.oracle_qwen_gates(n, Hv, _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                               _ptr(log_g), _ptr(beta))
+    if rc != 0:
+        raise ValueError(f"oracle_qwen_gates failed ({rc})")
+    return log_g, beta

@@ -218,6 +218,29 @@ int oracle_neumann_inverse(int n, const double* A, double* Tinv) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* Gates from raw projections                                               */
+/* ------------------------------------------------------------------------ */
+
+/* log(1 + e^x) without overflow: for x > 0 it is x + log(1 + e^-x). */
+static double softplus(double x) {
+    return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
+}
+
+int oracle_qwen_gates(long n, int Hv, const double* a, const double* b,
+                      const double* A_log, const double* dt_bias,
+                      double* log_g, double* beta) {
+    if (n < 0 || Hv <= 0) return -1;
+    if (n > 0 && (!a || !b || !A_log || !dt_bias || !log_g || !beta)) return -1;
+    for (long i = 0; i < n; ++i)
+        for (int h = 0; h < Hv; ++h) {
+            const long e = i * Hv + h;
+            log_g[e] = -exp(A_log[h]) * softplus(a[e] + dt_bias[h]);
+            beta[e] = 1.0 / (1.0 + exp(-b[e]));
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Chunked (WY) form with a direct right-hand-side solve                    */
 /* ------------------------------------------------------------------------ */
 

@@ -66,6 +66,15 @@ int oracle_unit_lower_inverse(int n, const double* A, double* Tinv);
  * nilpotent; kept only to pin the equivalence the pages rely on. */
 int oracle_neumann_inverse(int n, const double* A, double* Tinv);
 
+/* Qwen gates from raw projections ("Qwen3.5 Gated Delta Net NKI Kernel for
+ * AWS Neuron", section "Correctness Contract": log g = -exp(A_log)
+ * softplus(a + dt_bias)); beta = 1 / (1 + exp(-b)), a reading (the pages do
+ * not spell beta out).  a, b, log_g, beta hold n rows of Hv values (value head
+ * innermost); A_log, dt_bias hold Hv values. */
+int oracle_qwen_gates(long n, int Hv, const double* a, const double* b,
+                      const double* A_log, const double* dt_bias,
+                      double* log_g, double* beta);
+
 #ifdef __cplusplus
 }
 #endif

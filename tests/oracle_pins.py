@@ -309,6 +309,45 @@ def pin_triangular_inverse(lib):
         assert np.max(np.abs(Tn - Ti)) < 1e-12
 
 
+def pin_qwen_gates(lib):
+    """Closed forms of log g = -exp(A_log) softplus(a + dt_bias) and beta = sigmoid(b)
+    ("Qwen3.5 Gated Delta Net NKI Kernel for AWS Neuron", "Correctness Contract")."""
+    A_log = np.array([0.0, 0.5, -2.0, 1.0])
+    dt_bias = np.array([0.3, -1.0, 2.0, 0.0])
+    # a + dt_bias = 0: softplus = ln 2
+    a = -dt_bias[None, :].copy()
+    b = np.zeros((1, 4))
+    lg, bt = oracle.qwen_gates(a, b, A_log, dt_bias, lib=lib)
+    assert np.allclose(lg[0], -np.exp(A_log) * np.log(2.0), rtol=1e-15, atol=0)
+    assert np.all(bt == 0.5)
+    # a + dt_bias = ln(e - 1): softplus = 1, so log g = -exp(A_log)
+    a = (np.log(np.e - 1.0) - dt_bias)[None, :]
+    b = np.array([[np.log(3.0), -np.log(3.0), 0.0, 0.0]])
+    lg, bt = oracle.qwen_gates(a, b, A_log, dt_bias, lib=lib)
+    assert np.allclose(lg[0], -np.exp(A_log), rtol=1e-14, atol=0)
+    assert np.allclose(bt[0, :2], [0.75, 0.25], rtol=1e-15, atol=0)
+    # far tails: softplus(x) -> x (x >> 0) and -> e^x (x << 0); no overflow
+    a = np.array([[60.0, -60.0, 800.0, -800.0]]) - dt_bias[None, :]
+    b = np.array([[800.0, -800.0, 40.0, -40.0]])
+    lg, bt = oracle.qwen_gates(a, b, A_log, dt_bias, lib=lib)
+    assert np.allclose(lg[0, [0, 2]], -np.exp(A_log[[0, 2]]) * np.array([60.0, 800.0]), rtol=1e-15)
+    assert np.allclose(lg[0, 1], -np.exp(A_log[1]) * np.exp(-60.0), rtol=1e-12)
+    assert lg[0, 3] <= 0.0 and lg[0, 3] > -1e-300
+    assert bt[0, 0] == 1.0 and 0.0 <= bt[0, 1] < 1e-300
+    assert np.isclose(bt[0, 2] + bt[0, 3], 1.0, rtol=0, atol=1e-16)
+    # random rows: log g <= 0, decreasing in a; beta in (0, 1), sigma(-b) = 1 - sigma(b)
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal((50, 4)) * 4
+    b = rng.standard_normal((50, 4)) * 4
+    lg, bt = oracle.qwen_gates(a, b, A_log, dt_bias, lib=lib)
+    lg2, bt2 = oracle.qwen_gates(a + 0.25, -b, A_log, dt_bias, lib=lib)
+    assert np.all(lg < 0) and np.all(lg2 < lg)
+    assert np.all((bt > 0) & (bt < 1)) and np.allclose(bt + bt2, 1.0, rtol=0, atol=1e-15)
+    # matches an independent formulation of softplus (numpy's logaddexp(0, x))
+    x = a + dt_bias[None, :]
+    assert np.allclose(lg, -np.exp(A_log)[None, :] * np.logaddexp(0.0, x), rtol=1e-14, atol=0)
+
+
 PINS = [
     pin_identity_plumbing,
     pin_matrix_form,
@@ -324,4 +363,5 @@ PINS = [
     pin_normalisation,
     pin_chunked_equals_sequential,
     pin_triangular_inverse,
+    pin_qwen_gates,
 ]

@@ -128,3 +128,32 @@ def test_checkpointed_prefill_rejects_bad_arguments():
     # 4 slots of 1*2*64*64 fp32 = 131072 bytes: one byte short of hT's start
     # still overlaps; the call is then rejected before any launch
     assert prefill_ckpt(P(), 32, ck=fake(6, -131072 + 16)) == 7
+
+
+def prefill_gated(prob, every=0, ck=None, A_log=fake(9), dt_bias=fake(10), o=fake(7), a=fake(3)):
+    return B.lib().gdn_chunk_prefill_gated(ctypes.byref(prob), fake(0), fake(1), fake(2), a,
+                                           fake(4), A_log, dt_bias, None, fake(6), o, ck, every,
+                                           None, 0, None)
+
+
+def decode_gated(prob, A_log=fake(9), dt_bias=fake(10), st=fake(5)):
+    return B.lib().gdn_decode_step_gated(ctypes.byref(prob), fake(0), fake(1), fake(2), fake(3),
+                                         fake(4), A_log, dt_bias, st, fake(7), None)
+
+
+def test_gated_entry_points_reject_bad_arguments():
+    assert prefill_gated(P(Hv=3)) == 2
+    assert prefill_gated(P(), A_log=None) == 1
+    assert prefill_gated(P(), dt_bias=None) == 1
+    assert prefill_gated(P(), a=None) == 1
+    assert prefill_gated(P(), every=-32) == 2
+    assert prefill_gated(P(), every=48) == 2            # not a multiple of chunk 32
+    assert prefill_gated(P(), every=0, ck=fake(8)) == 2  # slots without an interval
+    assert prefill_gated(P(), every=32, ck=None) == 1
+    assert prefill_gated(P(), A_log=fake(9, 4)) == 4
+    assert prefill_gated(P(), A_log=fake(7, 64)) == 7   # gate parameters inside o
+    assert prefill_gated(P(), o=fake(10)) == 7          # o over dt_bias
+    assert decode_gated(P(T=1), A_log=None) == 1
+    assert decode_gated(P(T=1), dt_bias=fake(10, 8)) == 4
+    assert decode_gated(P(T=1), st=fake(9)) == 7        # state over A_log
+    assert decode_gated(P(T=2)) == 2

@@ -1,0 +1,134 @@
+"""GPU parity of the fused gate prologue (gdn_chunk_prefill_gated,
+gdn_decode_step_gated): the kernels form log g = -exp(A_log) softplus(a + dt_bias)
+and beta = sigmoid(b) from the raw projections.  Expected values: the oracle's
+gate function (pinned on its own) feeding the oracle recurrence."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_common import (NTHREADS, assert_parity, dev, dev32, host, run_oracle, say, torch_mod)
+from linear_attention_recurrence_04_amd import binding as gdn
+from linear_attention_recurrence_04_amd import inputs as gi
+
+pytestmark = pytest.mark.gpu
+
+
+def with_gates(inp, rg):
+    """Replace log_g and beta of an input dict by the oracle's gates of rg."""
+    lg, bt = oracle.qwen_gates(rg["a"], rg["b"], rg["A_log"], rg["dt_bias"])
+    out = dict(inp)
+    out["log_g"], out["beta"] = lg, bt
+    return out
+
+
+def run_gated(inp, rg, dtype, chunk, every=0):
+    torch = torch_mod()
+    q, k, v = dev(inp["q"], dtype), dev(inp["k"], dtype), dev(inp["v"], dtype)
+    h = None if inp["h0"] is None else dev32(inp["h0"])
+    res = gdn.gdn_chunk_prefill_gated(q, k, v, dev32(rg["a"]), dev32(rg["b"]), dev32(rg["A_log"]),
+                                      dev32(rg["dt_bias"]), h, ckpt_every=every, chunk=chunk)
+    torch.cuda.synchronize()
+    return res
+
+
+CASES = [  # (B, T, Hk, Hv, d, chunk, dtype)
+    (1, 100, 1, 2, 64, 32, "f32"),
+    (2, 77, 2, 4, 64, 16, "f32"),
+    (1, 200, 1, 3, 128, 64, "bf16"),     # MFMA path
+    (2, 130, 2, 6, 128, 64, "bf16"),     # MFMA path, GQA, ragged
+    (1, 129, 1, 3, 128, 32, "bf16"),     # generic bf16 path
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}_T{c[1]}_{c[2]}x{c[3]}_d{c[4]}_C{c[5]}_{c[6]}"
+                                             for c in CASES])
+def test_gated_prefill_matches_oracle(case):
+    torch = torch_mod()
+    B, T, Hk, Hv, d, C, dtype = case
+    say(f"gated prefill {case}")
+    inp = gi.custom_prefill(B, T, Hk, Hv, d, d, seed=31, dtype=dtype, gate="qwen", h0="normal")
+    rg = gi.make_raw_gates((B, T), Hv, seed=31)
+    o, hT, none = run_gated(inp, rg, dtype, C)
+    assert none is None
+    ref = with_gates(inp, rg)
+    o_ref, h_ref = run_oracle(ref)
+    assert_parity(host(o), o_ref, host(hT), h_ref, dtype, f"gated {case}")
+    # with checkpoints: o and hT unchanged, the last slot is hT
+    o2, h2, ck = run_gated(inp, rg, dtype, C, every=2 * C)
+    assert torch.equal(o2, o) and torch.equal(h2, hT) and torch.equal(ck[:, -1], hT)
+
+
+def test_gated_prefill_extreme_projections():
+    """Projections far in both tails: softplus overflow branch, g -> 1 and g -> 0,
+    beta -> 0 and 1; everything stays finite and matches the oracle."""
+    B, T, Hk, Hv, d = 1, 96, 1, 4, 64
+    inp = gi.custom_prefill(B, T, Hk, Hv, d, d, seed=5, dtype="f32", h0="normal")
+    rg = gi.make_raw_gates((B, T), Hv, seed=5)
+    rg["a"][:, ::3] = 60.0
+    rg["a"][:, 1::3] = -60.0
+    rg["b"][:, ::4] = 40.0
+    rg["b"][:, 1::4] = -40.0
+    o, hT, _ = run_gated(inp, rg, "f32", 32)
+    assert np.all(np.isfinite(host(o))) and np.all(np.isfinite(host(hT)))
+    o_ref, h_ref = run_oracle(with_gates(inp, rg))
+    assert_parity(host(o), o_ref, host(hT), h_ref, "f32", "extreme gates")
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_gated_decode_matches_oracle(dtype, d):
+    torch = torch_mod()
+    B, Hk, Hv, steps = 3, 2, 6, 4
+    say(f"gated decode {dtype} d={d}")
+    rng = np.random.default_rng(8)
+    state0 = (0.05 * rng.standard_normal((B, Hv, d, d))).astype(np.float32)
+    seq = gi.custom_prefill(B, steps, Hk, Hv, d, d, seed=9, dtype=dtype, gate="qwen")
+    rg = gi.make_raw_gates((B, steps), Hv, seed=9)
+    state = dev32(state0)
+    outs = []
+    for t in range(steps):
+        o = gdn.gdn_decode_step_gated(dev(seq["q"][:, t], dtype), dev(seq["k"][:, t], dtype),
+                                      dev(seq["v"][:, t], dtype), dev32(rg["a"][:, t]),
+                                      dev32(rg["b"][:, t]), dev32(rg["A_log"]),
+                                      dev32(rg["dt_bias"]), state)
+        outs.append(host(o))
+    torch.cuda.synchronize()
+    ref = with_gates(dict(seq, h0=state0), rg)
+    o_ref, h_ref = run_oracle(ref)
+    assert_parity(np.stack(outs, axis=1), o_ref, host(state), h_ref, dtype, f"gated decode {dtype}")
+
+
+def test_qwen27b_gated_full_size():
+    """27B prefill workload with raw gates (MFMA path): group 11 against the
+    oracle; one 27B decode step (B=64) with raw gates on every head."""
+    torch = torch_mod()
+    p = gi.QWEN27B_PREFILL
+    say(f"{p.name}: gated")
+    inp = gi.make_prefill(p, 0)
+    rg = gi.make_raw_gates((p.B, p.T), p.Hv, seed=0)
+    o, hT, _ = run_gated(inp, rg, "bf16", p.chunk)
+    o, hT = host(o), host(hT)
+    r = p.Hv // p.Hk
+    hk = 11
+    hs = slice(hk * r, (hk + 1) * r)
+    lg, bt = oracle.qwen_gates(rg["a"][:, :, hs], rg["b"][:, :, hs], rg["A_log"][hs],
+                               rg["dt_bias"][hs])
+    say(f"  oracle key head {hk}")
+    o_ref, h_ref = oracle.gdn_sequential(inp["q"][:, :, hk:hk + 1], inp["k"][:, :, hk:hk + 1],
+                                         inp["v"][:, :, hs], lg, bt, inp["h0"][:, hs], nthreads=r)
+    assert_parity(o[:, :, hs], o_ref, hT[:, hs], h_ref, "bf16", f"{p.name} gated group {hk}")
+
+    d = gi.QWEN27B_DECODE
+    say(f"{d.name}: one gated step, every head")
+    state0 = gi.make_decode_state(d, 0)
+    st = gi.make_decode_steps(d, 0, steps=1)
+    rgd = gi.make_raw_gates((d.B,), d.Hv, seed=1)
+    state = dev32(state0)
+    od = gdn.gdn_decode_step_gated(dev(st["q"][0], "bf16"), dev(st["k"][0], "bf16"),
+                                   dev(st["v"][0], "bf16"), dev32(rgd["a"]), dev32(rgd["b"]),
+                                   dev32(rgd["A_log"]), dev32(rgd["dt_bias"]), state)
+    torch.cuda.synchronize()
+    lgd, btd = oracle.qwen_gates(rgd["a"], rgd["b"], rgd["A_log"], rgd["dt_bias"])
+    o_ref, h_ref = oracle.gdn_sequential(st["q"][0][:, None], st["k"][0][:, None],
+                                         st["v"][0][:, None], lgd[:, None], btd[:, None], state0,
+                                         nthreads=NTHREADS)
+    assert_parity(host(od)[:, None], o_ref, host(state), h_ref, "bf16", f"{d.name} gated step")

@@ -53,6 +53,11 @@ MUTANTS = {
                                   "for (int s = 0; s < rr; ++s) {\n                            double dot")],
     "tri_inverse_sign": [("Tinv[i * n + c] -= aij * Tinv[j * n + c];",
                           "Tinv[i * n + c] += aij * Tinv[j * n + c];")],
+    "gate_no_dt_bias": [("softplus(a[e] + dt_bias[h])", "softplus(a[e])")],
+    "gate_A_log_not_exponentiated": [("-exp(A_log[h]) * softplus", "-A_log[h] * softplus")],
+    "gate_softplus_overflow_branch": [("return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));",
+                                       "return log1p(exp(x));")],
+    "gate_beta_sign": [("beta[e] = 1.0 / (1.0 + exp(-b[e]));", "beta[e] = 1.0 / (1.0 + exp(b[e]));")],
     "neumann_one_factor_short": [("for (int span = 1; span < n; span *= 2) {",
                                   "for (int span = 2; span < n; span *= 2) {")],
 }

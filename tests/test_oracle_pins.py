@@ -70,3 +70,4 @@ def test_bad_gqa_ratio_rejected(oracle_lib):
     q, k, v, log_g, beta, _ = _inputs(rng, 1, 3, 2, 3, 4, 4)
     with pytest.raises(ValueError):
         oracle.gdn_sequential(q, k, v, log_g, beta, None, lib=oracle_lib)
+
