@@ -8,7 +8,8 @@ steps, fp32 state updated in place) is timed in the same run and reported
 under "decode" as state-update HBM GB/s and tokens/s.  The same prefill call
 storing a state checkpoint every 512 tokens (gdn_chunk_prefill_ckpt) is timed
 too and reported under "checkpoints", and the call that forms the gates from
-raw projections (gdn_chunk_prefill_gated) under "raw_gates".
+raw projections (gdn_chunk_prefill_gated) under "raw_gates", and decode with
+4 tokens per call (gdn_decode_multi) under "decode_multi".
 
 Inputs are seeded synthetic tensors already resident in HBM when the timed
 region starts.  Kernel time comes from HIP events recorded on the stream the
@@ -189,6 +190,38 @@ def bench_decode(torch, gdn, d, steps, warmup):
     return ms / steps
 
 
+def bench_decode_multi(torch, gdn, d, steps, warmup, tokens_per_call: int):
+    """ms per gdn_decode_multi call of `tokens_per_call` tokens per sequence, over
+    the same per-step inputs as the decode leg, grouped in calls."""
+    T = tokens_per_call
+    calls = max(steps // T, 1)
+    st = gi.make_decode_steps(d, 0, steps=calls * T)
+    dv = {}
+    for n in st:   # [calls*T, B, ...] -> [calls, B, T, ...], contiguous per call
+        x = torch.from_numpy(st[n]).cuda()
+        x = x.reshape((calls, T) + x.shape[1:]).transpose(1, 2).contiguous()
+        dv[n] = x.to(torch.bfloat16) if n in ("q", "k", "v") else x
+    state0 = torch.from_numpy(gi.make_decode_state(d, 0)).cuda()
+    state = state0.clone()
+    out = torch.empty((d.B, T, d.Hv, d.dv), dtype=torch.bfloat16, device="cuda")
+    idx = [0]
+
+    def call():
+        c = idx[0]
+        gdn.gdn_decode_multi(dv["q"][c], dv["k"][c], dv["v"][c], dv["log_g"][c], dv["beta"][c],
+                             state, out=out)
+        idx[0] = (c + 1) % calls
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    state.copy_(state0)
+    idx[0] = 0
+    log(f"decode, {T} tokens per call: timing {calls} calls")
+    ms = time_stream(torch, call, calls)
+    return ms / calls, calls
+
+
 def cpu_baseline(p, sample_tokens: int):
     """The oracle as it stands, on the first `sample_tokens` tokens of the
     prefill workload (all heads), threaded over (b, h) on the host cores."""
@@ -213,6 +246,10 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the plain prefill and decode calls (profiling runs, where "
+                         "the checkpoint, raw-gate and multi-token legs would mix into the "
+                         "same kernels' statistics)")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
                     help="restrict to one half (profiling runs); 'copy' runs only the plain "
                          "copy kernel used to calibrate HBM byte counters")
@@ -282,6 +319,7 @@ def main():
             "avg_launch_us": round(ms * 1e3, 2), "source_hash": src,
         }
         log(f"prefill: {ms:.3f} ms/call, {result['value']:.0f} tok/s, {gbps:.1f} GB/s, {tflops:.2f} TFLOP/s")
+    if args.only in ("all", "prefill") and not args.no_extras:
         # the same call storing a state checkpoint every 512 tokens (32 slots)
         every = 512
         ms_c, _ = bench_prefill(torch, gdn, p, args.steps, args.warmup, ckpt_every=every)
@@ -325,6 +363,22 @@ def main():
             result["value"] = result["decode"]["tokens_per_s"]
             result["unit"] = "tokens/s (decode)"
             result["ms_per_step"] = round(ms_d, 5)
+    if args.only in ("all", "decode") and not args.no_extras:
+        # several tokens per call (speculative verification): the state is read
+        # and written once per call
+        Tm = 4
+        ms_m, calls = bench_decode_multi(torch, gdn, d, args.decode_steps, min(args.warmup, 10) or 1, Tm)
+        tok_bytes = d.B * Tm * (2 * d.Hk * d.dk * 2 + 2 * d.Hv * d.dv * 2 + 8 * d.Hv)
+        nb_m = 2 * d.B * d.Hv * d.dk * d.dv * 4 + tok_bytes
+        result["decode_multi"] = {
+            "tokens_per_call": Tm, "calls": calls, "us_per_call": round(ms_m * 1e3, 3),
+            "tokens_per_s": round(d.B * Tm / (ms_m * 1e-3), 1),
+            "speedup_vs_single_steps": round(Tm * ms_d / ms_m, 3),
+            "hbm_GBps": round(nb_m / (ms_m * 1e-3) / 1e9, 2),
+            "algorithmic_bytes_per_call": nb_m,
+        }
+        log(f"decode, {Tm} tokens per call: {ms_m * 1e3:.2f} us/call, "
+            f"{result['decode_multi']['tokens_per_s']:.0f} tok/s")
 
     if not args.no_cpu_baseline and args.only in ("all", "prefill"):
         log("cpu baseline: oracle on a bounded sample")

@@ -177,6 +177,40 @@ gdn_status gdn_decode_step(const gdn_problem* problem,
                            float* state, void* o, void* hip_stream);
 
 /*
+ * Multi-token decode: problem->T >= 0 tokens per sequence applied in order to
+ * a state that stays on chip for the whole call, for speculative or
+ * multi-token-prediction verification and small continuous-batching steps
+ * (the serving pages leave continuous batching, speculative decoding and
+ * native multi-token prediction to follow-up work: "Add Qwen3.6-27B hybrid
+ * DeltaNet/GQA contrib model and vLLM serving path", summary section "Known
+ * limitations and follow-ups", and its GitHub page, "Notes and Limitations").
+ * Exactly the token recurrence above, one token after another, with the
+ * decode step's fused single pass per token.
+ *
+ *   q, k     [B, T, Hk, dk]   dtype
+ *   v        [B, T, Hv, dv]   dtype
+ *   log_g    [B, T, Hv]       fp32 (or the raw projection a, see below)
+ *   beta     [B, T, Hv]       fp32 (or the raw projection b)
+ *   A_log, dt_bias  [Hv] fp32, or both NULL.  When given, log_g and beta hold
+ *            the raw projections and the gates are formed as in
+ *            gdn_chunk_prefill_gated.  Exactly one of them NULL:
+ *            GDN_ERR_NULL_POINTER.
+ *   state    [B, Hv, dk, dv]  fp32, read and overwritten in place (the state
+ *            after the last token)
+ *   o        [B, T, Hv, dv]   dtype, written
+ *   states   [B, T, Hv, dk, dv] fp32 state after every token (what a verifier
+ *            rolls back to when it accepts only a prefix of the draft), or
+ *            NULL.  It may not overlap any other argument.
+ * problem->chunk is ignored.  T == 0 leaves everything unchanged.  With T == 1
+ * and states == NULL this is gdn_decode_step.
+ */
+gdn_status gdn_decode_multi(const gdn_problem* problem,
+                            const void* q, const void* k, const void* v,
+                            const float* log_g, const float* beta,
+                            const float* A_log, const float* dt_bias,
+                            float* state, void* o, float* states, void* hip_stream);
+
+/*
  * Fused gate prologue.  The two variants below take the gate projections of
  * the model instead of log g and beta, and form the gates inside the kernels:
  *

@@ -68,6 +68,8 @@ def lib():
                                           ctypes.c_int32, vp, sz, vp]
     L.gdn_decode_step_gated.restype = ctypes.c_int
     L.gdn_decode_step_gated.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
+    L.gdn_decode_multi.restype = ctypes.c_int
+    L.gdn_decode_multi.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, vp]
     L.gdn_decode_step.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [pp, vp, vp, vp, fp, fp, fp, vp, vp]
     _lib = L
@@ -104,7 +106,8 @@ def gdn_chunk_prefill_variant(problem: GdnProblem) -> str:
 # kernel variant -> (kernel symbol, arithmetic, source files under csrc/)
 VARIANTS = {
     "generic_f32": ("prefill_generic_kernel", "fp32-valu", ("prefill_generic.hip",)),
-    "mfma_bf16": ("chunk_prep_kernel+chunk_scan_kernel", "bf16-mfma", ("prefill_mfma.hip",)),
+    "mfma_bf16": ("chunk_prep_kernel+chunk_scan_kernel", "bf16-mfma",
+                  ("prefill_mfma.hip", "prefill_mfma_common.h", "prefill_prep.inc")),
 }
 
 
@@ -347,3 +350,43 @@ def gdn_decode_step_gated(q, k, v, a, b, A_log, dt_bias, state, *, qk_l2norm: bo
                                      _stream(stream))
     _check(st)
     return out
+
+
+def gdn_decode_multi(q, k, v, log_g, beta, state, *, A_log=None, dt_bias=None,
+                     want_states: bool = False, qk_l2norm: bool = True, q_scale: float = 1.0,
+                     out=None, states=None, stream=None):
+    """T decode tokens per sequence in one call.  q, k [B,T,Hk,d]; v [B,T,Hv,d];
+    log_g, beta [B,T,Hv] fp32 (raw projections a, b when A_log and dt_bias
+    [Hv] are given); state [B,Hv,d,d] fp32 updated in place.  Returns
+    (o [B,T,Hv,d], states [B,T,Hv,d,d] or None): the state after every token."""
+    torch = _torch()
+    _need(q, "q")
+    dt = _dtype_code(q)
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    _need(k, "k", q.dtype, q.shape)
+    _need(v, "v", q.dtype, (B, T, Hv, dv))
+    _need(log_g, "log_g", torch.float32, (B, T, Hv))
+    _need(beta, "beta", torch.float32, (B, T, Hv))
+    _need(state, "state", torch.float32, (B, Hv, dk, dv))
+    if (A_log is None) != (dt_bias is None):
+        raise ValueError("A_log and dt_bias go together")
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, (Hv,))
+        _need(dt_bias, "dt_bias", torch.float32, (Hv,))
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(out, "out", q.dtype, (B, T, Hv, dv))
+    if states is None and want_states:
+        states = torch.empty((B, T, Hv, dk, dv), dtype=torch.float32, device=q.device)
+    elif states is not None:
+        _need(states, "states", torch.float32, (B, T, Hv, dk, dv))
+    prob = make_problem(B, T, Hk, Hv, dk, dv, chunk=0, dtype=dt, qk_l2norm=qk_l2norm,
+                        q_scale=q_scale)
+    st = lib().gdn_decode_multi(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g),
+                                _ptr(beta), _ptr(A_log), _ptr(dt_bias), _ptr(state), _ptr(out),
+                                _ptr(states) if states is not None and states.numel() else None,
+                                _stream(stream))
+    _check(st)
+    return out, states

@@ -11,6 +11,11 @@
 // the whole cost: the state is 4*dk*dv bytes per head against ~7*dk*dv flops,
 // so the kernel is bound by HBM bandwidth.
 //
+// T > 1 tokens per call (multi-token decode, speculative verification) run
+// the same pass once per token with the state kept in registers: it is read
+// once and written once per call, and optionally also stored after every
+// token (the per-token states a verifier rolls back to).
+//
 // Mapping: one workgroup of 256 threads per (b, h).  A thread owns a float4
 // column strip of D/RG rows (RG = row groups), held in VGPRs between the read
 // and the write; rows are interleaved so each wave load covers whole 512-byte
@@ -21,13 +26,13 @@
 
 namespace gdn {
 
-template <int D, typename TIn>
+template <int D, typename TIn, bool MULTI>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ log_g, const float* __restrict__ beta,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias,
-    float* __restrict__ state, TIn* __restrict__ o,
-    int Hk, int Hv, int l2norm, float q_scale) {
+    float* __restrict__ state, TIn* __restrict__ o, float* __restrict__ states,
+    int T, int Hk, int Hv, int l2norm, float q_scale) {
     constexpr int NT = 256;
     constexpr int CG = D / 4;     // float4 column groups per row
     constexpr int RG = NT / CG;   // row groups
@@ -56,10 +61,16 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int i = 0; i < RPT; ++i)
         s[i] = *reinterpret_cast<const float4*>(S + (size_t)(rg + RG * i) * D + 4 * cg);
 
+    const int NTOK = MULTI ? T : 1;   // a single step compiles to straight-line code
+    for (int t = 0; t < NTOK; ++t) {
+    if (t > 0) __syncthreads();   // the previous token is done with kh, qh, dl
+    const size_t bt_idx = (size_t)b * T + t;   // (sequence, token)
+    const size_t row = bt_idx * Hv + h;        // (sequence, token, value head)
+
     // 2. q, k of the key head, normalised in fp32
     float kv = 0.f, qv = 0.f;
     if (tid < D) {
-        const size_t off = ((size_t)b * Hk + hk) * D + tid;
+        const size_t off = (bt_idx * Hk + hk) * D + tid;
         kv = to_f32(k[off]);
         qv = to_f32(q[off]);
     }
@@ -108,7 +119,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     __syncthreads();
 
     // 4. column totals, delta and the output (one thread per column)
-    float lgv = log_g[bh], bt = beta[bh];
+    float lgv = log_g[row], bt = beta[row];
     if (A_log) {   // raw projections a, b
         const int h = bh % Hv;
         lgv = raw_log_decay(lgv, A_log[h], dt_bias[h]);
@@ -125,14 +136,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         float kq = 0.f;
 #pragma unroll
         for (int w = 0; w < (D + 63) / 64; ++w) kq += wsum[w][2];
-        const float vj = to_f32(v[(size_t)bh * D + tid]);
+        const float vj = to_f32(v[row * D + tid]);
         const float delta = bt * (vj - g * a);
         dl[tid] = delta;
-        o[(size_t)bh * D + tid] = from_f32<TIn>(q_scale * (g * c + delta * kq));
+        o[row * D + tid] = from_f32<TIn>(q_scale * (g * c + delta * kq));
     }
     __syncthreads();
 
-    // 5. S <- g S + k delta^T, written back over the same addresses
+    // 5. S <- g S + k delta^T (and the per-token state when asked for)
     const float4 d4 = *reinterpret_cast<const float4*>(&dl[4 * cg]);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -142,18 +153,42 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         n.y = g * s[i].y + kr * d4.y;
         n.z = g * s[i].z + kr * d4.z;
         n.w = g * s[i].w + kr * d4.w;
-        *reinterpret_cast<float4*>(S + (size_t)(rg + RG * i) * D + 4 * cg) = n;
+        if (MULTI)
+            s[i] = n;
+        else   // a single step writes back over the same addresses at once
+            *reinterpret_cast<float4*>(S + (size_t)(rg + RG * i) * D + 4 * cg) = n;
+    }
+    if (MULTI && states) {
+        float* St = states + row * D * D;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            *reinterpret_cast<float4*>(St + (size_t)(rg + RG * i) * D + 4 * cg) = s[i];
+    }
+    }   // tokens
+
+    if (MULTI) {   // the state back over the same addresses
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            *reinterpret_cast<float4*>(S + (size_t)(rg + RG * i) * D + 4 * cg) = s[i];
     }
 }
 
 template <int D, typename TIn>
 static hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const int blocks = a.B * a.Hv;
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_step_kernel<D, TIn>), dim3(blocks), dim3(256), 0, stream,
-                       static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                       static_cast<const TIn*>(a.v), a.log_g, a.beta, a.A_log, a.dt_bias, a.state,
-                       static_cast<TIn*>(a.o), a.Hk, a.Hv, a.l2norm, a.q_scale);
+    if (blocks == 0 || a.T == 0) return hipSuccess;
+    if (a.T == 1 && !a.states)
+        hipLaunchKernelGGL((decode_step_kernel<D, TIn, false>), dim3(blocks), dim3(256), 0, stream,
+                           static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                           static_cast<const TIn*>(a.v), a.log_g, a.beta, a.A_log, a.dt_bias,
+                           a.state, static_cast<TIn*>(a.o), nullptr, 1, a.Hk, a.Hv, a.l2norm,
+                           a.q_scale);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<D, TIn, true>), dim3(blocks), dim3(256), 0, stream,
+                           static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                           static_cast<const TIn*>(a.v), a.log_g, a.beta, a.A_log, a.dt_bias,
+                           a.state, static_cast<TIn*>(a.o), a.states, a.T, a.Hk, a.Hv, a.l2norm,
+                           a.q_scale);
     return hipGetLastError();
 }
 

@@ -31,12 +31,14 @@ bool overlaps(Range a, Range b) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Shared checks of the problem description.  `decode` selects the decode rules.
-gdn_status check_problem(const gdn_problem* p, bool decode) {
+// Shared checks of the problem description.  `decode` selects the decode rules
+// (T == 1, chunk ignored); `multi` the multi-token decode rules (any T >= 0,
+// chunk ignored).
+gdn_status check_problem(const gdn_problem* p, bool decode, bool multi = false) {
     if (!p) return GDN_ERR_NULL_POINTER;
     if (p->B < 0 || p->T < 0 || p->Hk < 1 || p->Hv < 1) return GDN_ERR_BAD_SHAPE;
     if (p->Hv % p->Hk != 0) return GDN_ERR_BAD_SHAPE;
-    if (decode && p->T != 1) return GDN_ERR_BAD_SHAPE;
+    if (decode && !multi && p->T != 1) return GDN_ERR_BAD_SHAPE;
     if (p->dk != p->dv) return GDN_ERR_UNSUPPORTED;
     if (p->dk != 64 && p->dk != 128) return GDN_ERR_UNSUPPORTED;
     if (p->dtype != GDN_DTYPE_F32 && p->dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
@@ -218,36 +220,41 @@ gdn_status gdn_chunk_prefill_gated(const gdn_problem* p, const void* q, const vo
 
 namespace {
 
+// T tokens per sequence (1 for gdn_decode_step); `states` optional.
 gdn_status decode_impl(const gdn_problem* p, const void* q, const void* k, const void* v,
                        const float* log_g, const float* beta, const float* A_log,
-                       const float* dt_bias, float* state, void* o, void* hip_stream) {
-    if (p->B > 0 && (!q || !k || !v || !log_g || !beta || !state || !o))
-        return GDN_ERR_NULL_POINTER;
-    const void* ptrs[] = {q, k, v, log_g, beta, state, o, A_log, dt_bias};
+                       const float* dt_bias, float* state, void* o, float* states,
+                       void* hip_stream) {
+    const size_t BT = (size_t)p->B * p->T;
+    if (p->B > 0 && !state) return GDN_ERR_NULL_POINTER;
+    if (BT > 0 && (!q || !k || !v || !log_g || !beta || !o)) return GDN_ERR_NULL_POINTER;
+    const void* ptrs[] = {q, k, v, log_g, beta, state, o, A_log, dt_bias, states};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
     const size_t es = dsize(p);
-    const size_t B = (size_t)p->B;
     const size_t par_bytes = (size_t)p->Hv * sizeof(float);
-    const Range r_state = range_of(state, B * p->Hv * p->dk * p->dv * sizeof(float));
-    const Range r_o = range_of(o, B * p->Hv * p->dv * es);
-    const Range ins[] = {range_of(q, B * p->Hk * p->dk * es), range_of(k, B * p->Hk * p->dk * es),
-                         range_of(v, B * p->Hv * p->dv * es), range_of(log_g, B * p->Hv * 4),
-                         range_of(beta, B * p->Hv * 4), range_of(A_log, A_log ? par_bytes : 0),
+    const size_t s_bytes = (size_t)p->B * p->Hv * p->dk * p->dv * sizeof(float);
+    const Range r_state = range_of(state, s_bytes);
+    const Range r_o = range_of(o, BT * p->Hv * p->dv * es);
+    const Range r_sts = range_of(states, states ? s_bytes * p->T : 0);
+    const Range ins[] = {range_of(q, BT * p->Hk * p->dk * es), range_of(k, BT * p->Hk * p->dk * es),
+                         range_of(v, BT * p->Hv * p->dv * es), range_of(log_g, BT * p->Hv * 4),
+                         range_of(beta, BT * p->Hv * 4), range_of(A_log, A_log ? par_bytes : 0),
                          range_of(dt_bias, dt_bias ? par_bytes : 0)};
     for (const Range& in : ins)
-        if (overlaps(in, r_state) || overlaps(in, r_o)) return GDN_ERR_ALIAS;
-    if (overlaps(r_state, r_o)) return GDN_ERR_ALIAS;
-    if (p->B == 0) return GDN_OK;
+        if (overlaps(in, r_state) || overlaps(in, r_o) || overlaps(in, r_sts)) return GDN_ERR_ALIAS;
+    if (overlaps(r_state, r_o) || overlaps(r_sts, r_state) || overlaps(r_sts, r_o))
+        return GDN_ERR_ALIAS;
+    if (BT == 0) return GDN_OK;
 
     gdn::DecodeArgs a;
-    a.B = p->B; a.Hk = p->Hk; a.Hv = p->Hv; a.D = p->dk;
+    a.B = p->B; a.T = p->T; a.Hk = p->Hk; a.Hv = p->Hv; a.D = p->dk;
     a.bf16 = p->dtype == GDN_DTYPE_BF16;
     a.l2norm = p->qk_l2norm;
     a.q_scale = p->q_scale;
     a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
     a.A_log = A_log; a.dt_bias = dt_bias;
-    a.state = state; a.o = o;
+    a.state = state; a.o = o; a.states = states;
     const hipError_t err = gdn::launch_decode_step(a, static_cast<hipStream_t>(hip_stream));
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -261,7 +268,17 @@ gdn_status gdn_decode_step(const gdn_problem* p, const void* q, const void* k, c
                            void* hip_stream) {
     const gdn_status st = check_problem(p, true);
     if (st != GDN_OK) return st;
-    return decode_impl(p, q, k, v, log_g, beta, nullptr, nullptr, state, o, hip_stream);
+    return decode_impl(p, q, k, v, log_g, beta, nullptr, nullptr, state, o, nullptr, hip_stream);
+}
+
+gdn_status gdn_decode_multi(const gdn_problem* p, const void* q, const void* k, const void* v,
+                            const float* log_g, const float* beta, const float* A_log,
+                            const float* dt_bias, float* state, void* o, float* states,
+                            void* hip_stream) {
+    const gdn_status st = check_problem(p, true, true);
+    if (st != GDN_OK) return st;
+    if ((A_log == nullptr) != (dt_bias == nullptr)) return GDN_ERR_NULL_POINTER;
+    return decode_impl(p, q, k, v, log_g, beta, A_log, dt_bias, state, o, states, hip_stream);
 }
 
 gdn_status gdn_decode_step_gated(const gdn_problem* p, const void* q, const void* k,
@@ -271,7 +288,7 @@ gdn_status gdn_decode_step_gated(const gdn_problem* p, const void* q, const void
     const gdn_status st = check_problem(p, true);
     if (st != GDN_OK) return st;
     if (!A_log || !dt_bias) return GDN_ERR_NULL_POINTER;
-    return decode_impl(p, q, k, v, a, b, A_log, dt_bias, state, o, hip_stream);
+    return decode_impl(p, q, k, v, a, b, A_log, dt_bias, state, o, nullptr, hip_stream);
 }
 
 }  // extern "C"

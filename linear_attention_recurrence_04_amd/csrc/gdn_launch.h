@@ -8,7 +8,7 @@
 namespace gdn {
 
 struct DecodeArgs {
-    int B, Hk, Hv, D;
+    int B, T, Hk, Hv, D;   // T tokens per sequence (1 for a plain decode step)
     bool bf16;
     int l2norm;
     float q_scale;
@@ -17,6 +17,7 @@ struct DecodeArgs {
     const float *A_log, *dt_bias;  // [Hv] gate parameters, or null
     float* state;
     void* o;
+    float* states;   // [B, T, Hv, D, D] state after every token, or null
 };
 
 struct PrefillArgs {

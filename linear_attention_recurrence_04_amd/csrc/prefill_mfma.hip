@@ -40,427 +40,18 @@
 //    only K S, Delta and the update; they also store the output.  Four loader
 //    waves stream the inputs into double-buffered LDS with direct
 //    global -> LDS loads.
-#include "gdn_device.h"
-#include "gdn_launch.h"
+#include "prefill_mfma_common.h"
 
 namespace gdn {
 namespace mfma_prefill {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-
-constexpr int D = 128;      // head dim (dk = dv)
-constexpr int C = 64;       // chunk
-constexpr int NT = 256;     // threads per workgroup (both kernels)
-constexpr int SK = D + 8;   // padded row stride (elements) of [64][128] bf16 tiles
-constexpr int SC = C + 8;   // padded row stride of [*][64] bf16 tiles
-
-// Workspace record per (b, value head, chunk): T and P (64x64 bf16 in
-// operand order, compact images: see imgc) and the gate vectors (fp32):
-// grk, wrk, beta, Gamma_C (read with k) and grq (read with q).
-constexpr int IMG_BYTES = (32 * 32 + 32 * 64) * 2;   // 6144
-constexpr int WS_T = 0;
-constexpr int WS_P = IMG_BYTES;
-constexpr int WS_G = 2 * IMG_BYTES;
-constexpr int WS_GQ = WS_G + 4 * C * 4;
-constexpr int WS_REC = WS_GQ + C * 4;               // 13568 bytes
-
-// Contraction-index order inside each 32-wide k step.  A pair of accumulator
-// tiles (rows 32ks.., 32ks+16..) gives lane (g, n) the rows {4g..4g+3} and
-// {16+4g..16+4g+3}; a 16x16x32 operand gives lane (g, n) the logical
-// k = 8g..8g+7.  Storing the other operand's physical 4-group q
-// (k = 4q..4q+3) at logical offset kperm(q) makes the two agree.
-__host__ __device__ constexpr int kperm(int q) { return 8 * (q & 3) + 4 * (q >> 2); }
-// logical position of physical index p
-__device__ __forceinline__ int lpos(int p) { return (p & ~31) + kperm((p >> 2) & 7) + (p & 3); }
-
-__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ short bfbits(float f) {
-    return __builtin_bit_cast(short, static_cast<__bf16>(f));
-}
-__device__ __forceinline__ s16x4 pack4(f32x4 v) {
-    s16x4 r;
-    r[0] = bfbits(v[0]); r[1] = bfbits(v[1]); r[2] = bfbits(v[2]); r[3] = bfbits(v[3]);
-    return r;
-}
-// operand from an accumulator tile pair (lo = rows 4g.., hi = rows 16+4g..)
-__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
-    bf16x8 r;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        r[t] = static_cast<__bf16>(lo[t]);
-        r[4 + t] = static_cast<__bf16>(hi[t]);
-    }
-    return r;
-}
-__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-__device__ __forceinline__ s16x4 ld4(const uint16_t* p) { return *reinterpret_cast<const s16x4*>(p); }
-__device__ __forceinline__ uint4 mask4(uint4 x, bool keep) {
-    const uint32_t m = keep ? 0xffffffffu : 0u;
-    return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
-}
-// Sum over each row of 16 lanes with DPP moves: swap neighbours, swap pairs,
-// mirror within 8 lanes, mirror within 16 lanes.  Every lane of the row ends
-// with the row's sum.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float row16_sum(float x) {
-    x += dpp_mov<0xB1>(x);    // quad_perm [1, 0, 3, 2]
-    x += dpp_mov<0x4E>(x);    // quad_perm [2, 3, 0, 1]
-    x += dpp_mov<0x141>(x);   // row_half_mirror
-    x += dpp_mov<0x140>(x);   // row_mirror
-    return x;
-}
-// exp(x) through the hardware base-2 exponential (arguments here are <= 0)
-__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
-
-// Lower-triangular 16x16 tiles of a 64x64 matrix: (0,0) (1,0) (1,1) (2,0) ...
-__device__ __forceinline__ void tile_of(int idx, int& a, int& b) {
-    a = (idx >= 1) + (idx >= 3) + (idx >= 6);
-    b = idx - (a * (a + 1)) / 2;
-}
-__host__ __device__ constexpr int tile_a(int idx) { return (idx >= 1) + (idx >= 3) + (idx >= 6); }
-__host__ __device__ constexpr int tile_b(int idx) { return idx - (tile_a(idx) * (tile_a(idx) + 1)) / 2; }
-
-// T and P are read by the scan as 16-byte MFMA operands: rows 0..31 only at
-// logical columns 0..31 (their first k step; the rest is zero), rows 32..63
-// at all 64.  The image keeps just those: rows 0..31 as 64-byte rows, rows
-// 32..63 as 128-byte rows after them.  Chunk c (logical columns 8c..8c+7) of
-// row r sits at chunk c ^ 2((r >> 2) & 1) in the short rows and at
-// c ^ ((r >> 1) & 7) in the long ones, so that the 16 rows an operand read
-// touches fall in distinct LDS banks.  Element position of logical column L
-// in row r (L < 32 when r < 32):
-__host__ __device__ constexpr int imgc(int r, int L) {
-    return r < 32 ? r * 32 + 8 * ((L >> 3) ^ (((r >> 2) & 1) << 1)) + (L & 7)
-                  : 1024 + (r - 32) * 64 + 8 * ((L >> 3) ^ ((r >> 1) & 7)) + (L & 7);
-}
-// the same position in 16-byte units for logical chunk c
-__host__ __device__ constexpr int imgq(int r, int c) {
-    return r < 32 ? r * 4 + (c ^ (((r >> 2) & 1) << 1)) : 128 + (r - 32) * 8 + (c ^ ((r >> 1) & 7));
-}
-
-// ===========================================================================
-// prep: one workgroup per (b, key head, chunk).  k, q, their norms and the
-// two Gram products are formed once for the Hv / Hk value heads that share
-// the key head; the gates, A, T and P once per value head.
-// ===========================================================================
-
-constexpr int GH = 4;   // value heads prepared together (one per wave for the gates,
-                        // one per 16-lane group in the diagonal solve)
-
-// Lower-triangular 16x16 blocks of a 64x64 matrix, stored compactly:
-// diagonal and below (i >= j) at tl_idx, strictly below (i > k) at ab_idx.
-__host__ __device__ constexpr int tl_idx(int i, int j) { return i * (i + 1) / 2 + j; }
-__host__ __device__ constexpr int ab_idx(int i, int k) { return i * (i - 1) / 2 + k; }
-
-// k and q rows are needed only up to the Gram products; the triangular
-// factors of the group's value heads reuse their space.
-struct PrepSmem {
-    union {
-        struct {
-            uint16_t Kr[C][SK];       // raw k rows (bf16)
-            uint16_t Qr[C][SK];       // raw q rows
-        } in;
-        struct {
-            float AfT[GH][4][16][16];      // A diagonal blocks (fp32), transposed: [head][block][s][r]
-            uint16_t Ab[GH][6][16][16];    // A blocks below the diagonal (bf16)
-            uint16_t Tl[GH][10][16][16];   // T blocks on and below the diagonal (bf16)
-        } tri;
-    };
-    float rk[C], rq[C];
-    float gam[GH][C], bt[GH][C];
-};
-
-// Gating of one wave's five Gram tiles (tasks W, W + 4, .., W + 16: tasks
-// 0..9 are K K^T tiles, 10..19 Q K^T tiles) for the nh value heads of a
-// group, with the tile geometry known at compile time so that every LDS
-// read of a head is issued before its arithmetic.  Lane (g, n) holds
-// s = 16bb + 4g + t, r = 16a + n.  A goes to LDS (diagonal blocks fp32,
-// others bf16); P goes to the record of each head (rec0 + hh * rec_stride).
-template <int W>
-__device__ __forceinline__ void gate_tiles(PrepSmem& sm, const f32x4 (&gram)[5], int nh, int g, int n,
-                                           unsigned char* rec0, size_t rec_stride) {
-    f32x4 ks[4];
-    float rkr[4], rqr[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        ks[x] = *reinterpret_cast<const f32x4*>(&sm.rk[16 * x + 4 * g]);
-        rkr[x] = sm.rk[16 * x + n];
-        rqr[x] = sm.rq[16 * x + n];
-    }
-#pragma unroll 1
-    for (int hh = 0; hh < nh; ++hh) {
-        float gr[4], btr[4];
-        f32x4 gs[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            gr[x] = sm.gam[hh][16 * x + n];
-            btr[x] = sm.bt[hh][16 * x + n];
-            gs[x] = *reinterpret_cast<const f32x4*>(&sm.gam[hh][16 * x + 4 * g]);
-        }
-        uint16_t* Pg = reinterpret_cast<uint16_t*>(rec0 + hh * rec_stride + WS_P);
-#pragma unroll
-        for (int u = 0; u < 5; ++u) {
-            const int task = W + 4 * u;
-            const bool is_qk = task >= 10;
-            const int a = tile_a(is_qk ? task - 10 : task);
-            const int bb = tile_b(is_qk ? task - 10 : task);
-            const int r = 16 * a + n;
-            const float sr = is_qk ? rqr[a] : rkr[a] * btr[a];
-            f32x4 val;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int s2 = 16 * bb + 4 * g + t;
-                const bool keep = is_qk ? (s2 <= r) : (s2 < r);
-                const float x = exp_hw(gr[a] - gs[bb][t]) * sr * ks[bb][t] * gram[u][t];
-                val[t] = keep ? x : 0.f;
-            }
-            if (is_qk) {
-                const int q4 = 4 * bb + g;   // physical 4-group of s
-                *reinterpret_cast<s16x4*>(Pg + imgc(r, 32 * (q4 >> 3) + kperm(q4 & 7))) = pack4(val);
-                if (a == bb && (a == 0 || a == 2)) {  // upper neighbour read by the scan: zero
-                    const int qz = q4 + 4;
-                    const s16x4 z = {0, 0, 0, 0};
-                    *reinterpret_cast<s16x4*>(Pg + imgc(r, 32 * (qz >> 3) + kperm(qz & 7))) = z;
-                }
-            } else if (a == bb) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) sm.tri.AfT[hh][a][4 * g + t][n] = val[t];
-            } else {
-                *reinterpret_cast<s16x4*>(&sm.tri.Ab[hh][ab_idx(a, bb)][n][4 * g]) = pack4(val);
-            }
-        }
-    }
-}
-
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-    const float* __restrict__ log_g, const float* __restrict__ beta,
-    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
-    unsigned char* __restrict__ ws, int T, int NTc, int Hk, int Hv, int l2norm) {
-    __shared__ PrepSmem sm;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int g = lane >> 4;
-    const int n = lane & 15;
-
-    const int chunk = blockIdx.x % NTc;
-    const int bk = blockIdx.x / NTc;
-    const int b = bk / Hk;
-    const int hk = bk - b * Hk;
-    const int rr = Hv / Hk;
-    const int t0 = chunk * C;
-    const int L = min(C, T - t0);
-
-    // gate inputs of value head hk * rr + jg + w for t0 + lane (clamped row;
-    // padding rows get g = 1, beta = 0 below), fetched one group ahead
-    auto gate_in = [&](int jg, float& lgr, float& btr) __attribute__((always_inline)) {
-        const int j = min(jg + w, rr - 1);
-        const size_t gi = ((size_t)b * T + t0 + min(lane, L - 1)) * Hv + hk * rr + j;
-        lgr = log_g[gi];
-        btr = beta[gi];
-        if (A_log) {   // raw projections a, b
-            lgr = raw_log_decay(lgr, A_log[hk * rr + j], dt_bias[hk * rr + j]);
-            btr = raw_beta(btr);
-        }
-    };
-    float lg_next, bt_next;
-    gate_in(0, lg_next, bt_next);
-
-    // ---- stage raw q, k rows (rows >= L are zero) and their inverse norms
-    //      (16 lanes per row); all eight loads are issued first
-    u32x4 kv[4], qv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int r = (tid + NT * u) >> 4;
-        const int c8 = (tid & 15) * 8;
-        const size_t off = (((size_t)b * T + t0 + min(r, L - 1)) * Hk + hk) * D + c8;
-        kv[u] = *reinterpret_cast<const u32x4*>(k + off);
-        qv[u] = *reinterpret_cast<const u32x4*>(q + off);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int r = (tid + NT * u) >> 4;
-        const int c8 = (tid & 15) * 8;
-        const uint32_t m = (r < L) ? 0xffffffffu : 0u;
-        const u32x4 kx = kv[u] & m, qx = qv[u] & m;
-        *reinterpret_cast<u32x4*>(&sm.in.Kr[r][c8]) = kx;
-        *reinterpret_cast<u32x4*>(&sm.in.Qr[r][c8]) = qx;
-        float sk = 0.f, sq = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float k0 = __uint_as_float(kx[e] << 16), k1 = __uint_as_float(kx[e] & 0xffff0000u);
-            const float q0 = __uint_as_float(qx[e] << 16), q1 = __uint_as_float(qx[e] & 0xffff0000u);
-            sk += k0 * k0 + k1 * k1;
-            sq += q0 * q0 + q1 * q1;
-        }
-        sk = row16_sum(sk);
-        sq = row16_sum(sq);
-        if ((lane & 15) == 0) {
-            sm.rk[r] = l2norm ? inv_l2(sk) : 1.f;
-            sm.rq[r] = l2norm ? inv_l2(sq) : 1.f;
-        }
-    }
-    __syncthreads();
-
-    // ---- raw Gram tiles, computed transposed (s on the M side), kept in
-    //      registers: 10 of K K^T, 10 of Q K^T; wave w owns tasks w + 4u.
-    //      Lane (g, n) holds s = 16bb + 4g + t, r = 16a + n.
-    f32x4 gram[5];
-#pragma unroll
-    for (int u = 0; u < 5; ++u) {
-        const int task = w + 4 * u;
-        const bool is_qk = task >= 10;
-        int a, bb;
-        tile_of(is_qk ? task - 10 : task, a, bb);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* rowsB = is_qk ? &sm.in.Qr[16 * a + n][0] : &sm.in.Kr[16 * a + n][0];
-        bf16x8 opa[4], opb[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            opa[ks] = ld8(&sm.in.Kr[16 * bb + n][32 * ks + 8 * g]);
-            opb[ks] = ld8(rowsB + 32 * ks + 8 * g);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma32(opa[ks], opb[ks], acc);
-        gram[u] = acc;
-    }
-
-    for (int jg = 0; jg < rr; jg += GH) {
-        const int nh = min(GH, rr - jg);   // value heads in this group
-        // ---- gates of value heads jg .. jg + GH - 1 (wave w: head jg + w):
-        //      decay scan, then Gamma rk, exp(gamma_C - gamma) rk, Gamma rq,
-        //      beta, Gamma_C to the record.  Padding rows: g = 1, beta = 0.
-        const float lgr = lg_next, btr = bt_next;
-        if (jg + GH < rr) gate_in(jg + GH, lg_next, bt_next);
-        if (w < nh) {
-            const int h = hk * rr + jg + w;
-            float x = (lane < L) ? lgr : 0.f;
-            const float btv = (lane < L) ? btr : 0.f;
-#pragma unroll
-            for (int m = 1; m < 64; m <<= 1) {
-                const float y = __shfl_up(x, m, 64);
-                if (lane >= m) x += y;
-            }
-            sm.gam[w][lane] = x;
-            sm.bt[w][lane] = btv;
-            const float total = __shfl(x, 63, 64);
-            const float Gm = exp_hw(x);
-            const float rkv = sm.rk[lane];
-            float* gp = reinterpret_cast<float*>(ws + (((size_t)b * Hv + h) * NTc + chunk) * WS_REC + WS_G);
-            gp[0 * C + lane] = Gm * rkv;
-            gp[1 * C + lane] = exp_hw(total - x) * rkv;
-            gp[2 * C + lane] = btv;
-            gp[3 * C + lane] = exp_hw(total);
-            gp[4 * C + lane] = Gm * sm.rq[lane];
-        }
-        __syncthreads();   // k and q rows are dead from here: their space holds A and T
-
-        // ---- gate the Gram tiles for every head of the group: A (diagonal
-        //      blocks fp32, others bf16) to LDS, P straight to the record
-        {
-            unsigned char* rec0 = ws + (((size_t)b * Hv + hk * rr + jg) * NTc + chunk) * WS_REC;
-            const size_t rec_stride = (size_t)NTc * WS_REC;
-            switch (w) {
-                case 0: gate_tiles<0>(sm, gram, nh, g, n, rec0, rec_stride); break;
-                case 1: gate_tiles<1>(sm, gram, nh, g, n, rec0, rec_stride); break;
-                case 2: gate_tiles<2>(sm, gram, nh, g, n, rec0, rec_stride); break;
-                default: gate_tiles<3>(sm, gram, nh, g, n, rec0, rec_stride); break;
-            }
-        }
-        __syncthreads();
-
-        // ---- diagonal blocks: T_ww = (I + A_ww)^-1 by forward substitution.
-        //      Wave w solves block w for every head at once: lane (g, n) is
-        //      column n of head g.  Once row s of the column is final, its
-        //      multiples are removed from the rows below it.
-        {
-            const int hh = g;
-            float tc[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) tc[r] = (r == n) ? 1.f : 0.f;
-#pragma unroll
-            for (int s2 = 0; s2 < 15; ++s2) {
-                float col[16];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sm.tri.AfT[hh][w][s2][4 * x]);
-                    col[4 * x] = c4[0]; col[4 * x + 1] = c4[1]; col[4 * x + 2] = c4[2]; col[4 * x + 3] = c4[3];
-                }
-#pragma unroll
-                for (int r = s2 + 1; r < 16; ++r) tc[r] -= col[r] * tc[s2];
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.tri.Tl[hh][tl_idx(w, w)][r][n] = static_cast<uint16_t>(bfbits(tc[r]));
-        }
-        __syncthreads();
-
-        // ---- blocks below the diagonal in column block j = w, every head:
-        //      (I + A_ii) T_ij + sum_{k=j}^{i-1} A_ik T_kj = 0  =>  T_ij = -T_ii sum_k A_ik T_kj
-        {
-            const int j = w;
-            s16x4 tk[GH][4];   // T_kj as operand (accumulator layout), k = j..3
-#pragma unroll
-            for (int hh = 0; hh < GH; ++hh) {
-                s16x4 d;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) d[t] = static_cast<short>(sm.tri.Tl[hh][tl_idx(j, j)][4 * g + t][n]);
-                tk[hh][0] = d;
-            }
-#pragma unroll
-            for (int di = 1; di < 4; ++di) {
-                const int i = j + di;
-                if (i < 4) {
-#pragma unroll
-                    for (int hh = 0; hh < GH; ++hh) {
-                        if (hh < nh) {
-                            f32x4 R = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                            for (int dk = 0; dk < di; ++dk)
-                                R = mfma16(ld4(&sm.tri.Ab[hh][ab_idx(i, j + dk)][n][4 * g]), tk[hh][dk], R);
-                            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                            const f32x4 Tij = mfma16(ld4(&sm.tri.Tl[hh][tl_idx(i, i)][n][4 * g]), pack4(-R), zero);
-                            tk[hh][di] = pack4(Tij);
-#pragma unroll
-                            for (int t = 0; t < 4; ++t)
-                                sm.tri.Tl[hh][tl_idx(i, j)][4 * g + t][n] = static_cast<uint16_t>(tk[hh][di][t]);
-                        }
-                    }
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- T of every head to its record in operand order (8-byte groups,
-        //      permuted per 32); blocks above the diagonal are zero.  The next
-        //      group rewrites A first and T only after its next barrier.
-        for (int hh = 0; hh < nh; ++hh) {
-            const int h = hk * rr + jg + hh;
-            uint16_t* Tg = reinterpret_cast<uint16_t*>(ws + (((size_t)b * Hv + h) * NTc + chunk) * WS_REC + WS_T);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = tid + NT * u;        // 1024 groups: row r, physical group Qg (16 per row)
-                const int r = e >> 4;
-                const int Qg = e & 15;
-                const int bi = r >> 4, bj = Qg >> 2;
-                if (r < 32 && Qg >= 8) continue;   // not in the image (zero)
-                uint2 val = make_uint2(0u, 0u);
-                if (bj <= bi) val = *reinterpret_cast<const uint2*>(&sm.tri.Tl[hh][tl_idx(bi, bj)][r & 15][4 * (Qg & 3)]);
-                *reinterpret_cast<uint2*>(Tg + imgc(r, 32 * (Qg >> 3) + kperm(Qg & 7))) = val;
-            }
-        }
-    }
-}
+// The prep kernel with the gates given; the same body with raw gate
+// projections is compiled in prefill_prep_raw.hip.
+#define PREP_KERNEL chunk_prep_kernel
+#define PREP_RAW false
+#include "prefill_prep.inc"
+#undef PREP_KERNEL
+#undef PREP_RAW
 
 // ===========================================================================
 // scan: one workgroup per (b, value head h, 32 state columns), in three roles:
@@ -942,10 +533,15 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
     const int prep_blocks = a.B * a.Hk * NTc;
     if (prep_blocks == 0) return hipSuccess;
     unsigned char* ws = static_cast<unsigned char*>(a.ws);
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3(prep_blocks), dim3(NT), 0, stream,
-                       static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k), a.log_g, a.beta,
-                       a.A_log, a.dt_bias, ws, a.T, NTc, a.Hk, a.Hv, a.l2norm);
-    hipError_t err = hipGetLastError();
+    hipError_t err;
+    if (a.A_log) {
+        err = launch_prep_raw(a, NTc, ws, stream);
+    } else {
+        hipLaunchKernelGGL(chunk_prep_kernel, dim3(prep_blocks), dim3(NT), 0, stream,
+                           static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k), a.log_g,
+                           a.beta, nullptr, nullptr, ws, a.T, NTc, a.Hk, a.Hv, a.l2norm);
+        err = hipGetLastError();
+    }
     if (err != hipSuccess) return err;
     const int scan_blocks = a.B * a.Hv * (D / BVS);
     const int remap = (scan_blocks % 8 == 0) ? 1 : 0;

@@ -157,3 +157,21 @@ def test_gated_entry_points_reject_bad_arguments():
     assert decode_gated(P(T=1), dt_bias=fake(10, 8)) == 4
     assert decode_gated(P(T=1), st=fake(9)) == 7        # state over A_log
     assert decode_gated(P(T=2)) == 2
+
+
+def decode_multi(prob, A_log=None, dt_bias=None, st=fake(5), sts=None, o=fake(7)):
+    return B.lib().gdn_decode_multi(ctypes.byref(prob), fake(0), fake(1), fake(2), fake(3),
+                                    fake(4), A_log, dt_bias, st, o, sts, None)
+
+
+def test_multi_token_decode_rejects_bad_arguments():
+    assert decode_multi(P(T=-1)) == 2
+    assert decode_multi(P(Hv=3)) == 2
+    assert decode_multi(P(T=4), A_log=fake(9)) == 1     # A_log without dt_bias
+    assert decode_multi(P(T=4), st=None) == 1
+    assert decode_multi(P(T=4), sts=fake(8, 8)) == 4
+    assert decode_multi(P(T=4), sts=fake(5, 4096)) == 7  # per-token states over the state
+    assert decode_multi(P(T=4), o=fake(8), sts=fake(8)) == 7
+    assert decode_multi(P(T=4, dk=32, dv=32)) == 3
+    # the chunk field is ignored by decode
+    assert decode_multi(P(T=4, chunk=48), st=None) == 1
