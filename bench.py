@@ -9,7 +9,8 @@ under "decode" as state-update HBM GB/s and tokens/s.  The same prefill call
 storing a state checkpoint every 512 tokens (gdn_chunk_prefill_ckpt) is timed
 too and reported under "checkpoints", and the call that forms the gates from
 raw projections (gdn_chunk_prefill_gated) under "raw_gates", and decode with
-4 tokens per call (gdn_decode_multi) under "decode_multi".
+4 tokens per call (gdn_decode_multi) under "decode_multi", and a packed batch
+of 8 sequences of different lengths (gdn_chunk_prefill_varlen) under "varlen".
 
 Inputs are seeded synthetic tensors already resident in HBM when the timed
 region starts.  Kernel time comes from HIP events recorded on the stream the
@@ -161,6 +162,38 @@ def bench_prefill(torch, gdn, p, steps, warmup, ckpt_every: int = 0, raw_gates: 
         f"{' with raw gates' if raw_gates else ''}: timing {steps} steps")
     ms = time_stream(torch, call, steps)
     return ms / steps, prob
+
+
+VARLEN_MIX = [4096, 3000, 2500, 2048, 1800, 1500, 900, 540]   # 16384 tokens, 8 sequences
+
+
+def bench_prefill_varlen(torch, gdn, p, steps, warmup):
+    """ms per packed call of the sequence mix VARLEN_MIX at the 27B head shape."""
+    log(f"varlen prefill {VARLEN_MIX}: generating inputs")
+    seqs = [gi.make_prefill(p, 100 + i, T=L) for i, L in enumerate(VARLEN_MIX)]
+    dev = {n: torch.from_numpy(np.concatenate([s[n][0] for s in seqs], axis=0)).cuda()
+           for n in ("q", "k", "v", "log_g", "beta")}
+    for n in ("q", "k", "v"):
+        dev[n] = dev[n].to(torch.bfloat16)
+    h0 = torch.from_numpy(np.concatenate([s["h0"] for s in seqs], axis=0)).cuda()
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(VARLEN_MIX)]), dtype=torch.int32, device="cuda")
+    total = int(sum(VARLEN_MIX))
+    out = torch.empty((total, p.Hv, p.dv), dtype=torch.bfloat16, device="cuda")
+    hT = torch.empty_like(h0)
+    prob = gdn.make_problem(len(VARLEN_MIX), max(VARLEN_MIX), p.Hk, p.Hv, p.dk, p.dv, chunk=p.chunk)
+    ws = torch.empty(max(gdn.gdn_chunk_prefill_workspace_bytes(prob), 1), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        gdn.gdn_chunk_prefill_varlen(dev["q"], dev["k"], dev["v"], dev["log_g"], dev["beta"], cu,
+                                     max(VARLEN_MIX), h0, chunk=p.chunk, out=out, hT=hT,
+                                     workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    log(f"varlen prefill: timing {steps} steps")
+    return time_stream(torch, call, steps) / steps
 
 
 def bench_decode(torch, gdn, d, steps, warmup):
@@ -341,6 +374,14 @@ def main():
             "gate_tensor_bytes_not_materialised": 2 * p.B * p.T * p.Hv * 4 * 2,
         }
         log(f"prefill with raw gates: {ms_g:.3f} ms/call ({(ms_g - ms) * 1e3:+.1f} us)")
+        # a packed batch of 8 sequences of different lengths, 16384 tokens in all
+        ms_v = bench_prefill_varlen(torch, gdn, p, args.steps, args.warmup)
+        result["varlen"] = {
+            "lengths": VARLEN_MIX, "ms_per_call": round(ms_v, 4),
+            "tokens_per_s": round(sum(VARLEN_MIX) / (ms_v * 1e-3), 1),
+            "vs_one_16384_token_sequence": round(ms / ms_v, 3),
+        }
+        log(f"varlen prefill: {ms_v:.3f} ms/call, {result['varlen']['tokens_per_s']:.0f} tok/s")
 
     if args.only in ("all", "decode"):
         ms_d = bench_decode(torch, gdn, d, args.decode_steps, min(args.warmup, 10) or 1)

@@ -177,6 +177,42 @@ gdn_status gdn_decode_step(const gdn_problem* problem,
                            float* state, void* o, void* hip_stream);
 
 /*
+ * Chunked prefill of a packed batch of sequences of different lengths (the
+ * continuous-batching form of context encoding, which the serving pages leave
+ * to follow-up work: "Add Qwen3.6-27B hybrid DeltaNet/GQA contrib model and
+ * vLLM serving path", summary, "Known limitations and follow-ups").  Every
+ * sequence is an independent gdn_chunk_prefill: its own chunks (the last one
+ * partial), its own initial and final state.
+ *
+ *   problem->B      number of sequences
+ *   problem->T      the longest sequence (sizes the launch and the workspace:
+ *                   gdn_chunk_prefill_workspace_bytes(problem) applies)
+ *   cu_seqlens      DEVICE int32 [B + 1]: sequence b is tokens
+ *                   cu_seqlens[b] .. cu_seqlens[b + 1] - 1 of the token axis;
+ *                   0 = cu_seqlens[0] <= ... <= cu_seqlens[B] = total_tokens
+ *                   and no sequence longer than problem->T.  These are not
+ *                   checked (they live on the device): values outside them are
+ *                   clamped into range, so memory stays in bounds, but results
+ *                   are then undefined.
+ *   total_tokens    length of the token axis, 0 .. 2^31 - 1
+ *   q, k            [total_tokens, Hk, dk]  dtype
+ *   v               [total_tokens, Hv, dv]  dtype
+ *   log_g, beta     [total_tokens, Hv]      fp32
+ *   h0, hT          [B, Hv, dk, dv] fp32 (NULL as in gdn_chunk_prefill)
+ *   o               [total_tokens, Hv, dv]  dtype; rows outside every
+ *                   sequence are left untouched
+ * A sequence of length 0 gets hT = h0.  The results of sequence b are bitwise
+ * those of gdn_chunk_prefill on that sequence alone.
+ */
+gdn_status gdn_chunk_prefill_varlen(const gdn_problem* problem, const int32_t* cu_seqlens,
+                                    int64_t total_tokens,
+                                    const void* q, const void* k, const void* v,
+                                    const float* log_g, const float* beta,
+                                    const float* h0, float* hT, void* o,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* hip_stream);
+
+/*
  * Multi-token decode: problem->T >= 0 tokens per sequence applied in order to
  * a state that stays on chip for the whole call, for speculative or
  * multi-token-prediction verification and small continuous-batching steps

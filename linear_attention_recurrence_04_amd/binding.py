@@ -70,6 +70,9 @@ def lib():
     L.gdn_decode_step_gated.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
     L.gdn_decode_multi.restype = ctypes.c_int
     L.gdn_decode_multi.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, vp]
+    L.gdn_chunk_prefill_varlen.restype = ctypes.c_int
+    L.gdn_chunk_prefill_varlen.argtypes = [pp, vp, ctypes.c_int64, vp, vp, vp, fp, fp, fp, fp, vp,
+                                           vp, sz, vp]
     L.gdn_decode_step.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [pp, vp, vp, vp, fp, fp, fp, vp, vp]
     _lib = L
@@ -390,3 +393,52 @@ def gdn_decode_multi(q, k, v, log_g, beta, state, *, A_log=None, dt_bias=None,
                                 _stream(stream))
     _check(st)
     return out, states
+
+
+def gdn_chunk_prefill_varlen(q, k, v, log_g, beta, cu_seqlens, max_seqlen: Optional[int] = None,
+                             h0=None, *, chunk: int = 64, qk_l2norm: bool = True,
+                             q_scale: float = 1.0, out=None, hT=None, workspace=None,
+                             stream=None):
+    """Chunked prefill of a packed batch of sequences of different lengths.
+    q, k [total, Hk, d]; v [total, Hv, d]; log_g, beta [total, Hv] fp32;
+    cu_seqlens int32 [N+1] on the GPU (sequence b = tokens cu[b] .. cu[b+1]-1);
+    h0 [N, Hv, d, d] fp32 or None.  ``max_seqlen`` (the longest sequence) sizes
+    the launch; when omitted it is read from cu_seqlens, which synchronises.
+    Returns (o [total, Hv, d], hT [N, Hv, d, d])."""
+    torch = _torch()
+    _need(q, "q")
+    dt = _dtype_code(q)
+    total, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    _need(k, "k", q.dtype, q.shape)
+    _need(v, "v", q.dtype, (total, Hv, dv))
+    _need(log_g, "log_g", torch.float32, (total, Hv))
+    _need(beta, "beta", torch.float32, (total, Hv))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of N+1 offsets")
+    N = cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if N > 0 else 0
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (N, Hv, dk, dv))
+    if out is None:
+        out = torch.empty((total, Hv, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(out, "out", q.dtype, (total, Hv, dv))
+    if hT is None:
+        hT = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=q.device)
+    else:
+        _need(hT, "hT", torch.float32, (N, Hv, dk, dv))
+    prob = make_problem(N, max_seqlen, Hk, Hv, dk, dv, chunk=chunk, dtype=dt,
+                        qk_l2norm=qk_l2norm, q_scale=q_scale)
+    need = gdn_chunk_prefill_workspace_bytes(prob)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().gdn_chunk_prefill_varlen(ctypes.byref(prob), _ptr(cu_seqlens), int(total), _ptr(q),
+                                        _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta), _ptr(h0),
+                                        _ptr(hT), _ptr(out), _ptr(workspace), ws_bytes,
+                                        _stream(stream))
+    _check(st)
+    return out, hT

@@ -113,13 +113,17 @@ namespace {
 // gdn_chunk_prefill with optional checkpoints (h_ckpt == NULL and
 // ckpt_every == 0 for none; the caller has checked ckpt_every) and optional
 // raw gates (A_log, dt_bias non-null: log_g, beta hold the projections a, b).
+// Packed variable-length batches pass cu (device [B + 1]) and the length
+// `total` of the token axis; otherwise cu is NULL and total = B * T.
 gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, const void* v,
                         const float* log_g, const float* beta, const float* A_log,
                         const float* dt_bias, const float* h0, float* hT, void* o,
                         float* h_ckpt, int ckpt_every, void* workspace,
-                        size_t workspace_bytes, void* hip_stream) {
+                        size_t workspace_bytes, void* hip_stream,
+                        const int32_t* cu = nullptr, long long total = -1) {
     const size_t es = dsize(p);
-    const size_t BT = (size_t)p->B * p->T;
+    if (total < 0) total = (long long)p->B * p->T;
+    const size_t BT = (size_t)total;
     const size_t qk_bytes = BT * p->Hk * p->dk * es;
     const size_t v_bytes = BT * p->Hv * p->dv * es;
     const size_t g_bytes = BT * p->Hv * sizeof(float);
@@ -129,7 +133,7 @@ gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, cons
 
     if (BT > 0 && (!q || !k || !v || !log_g || !beta || !o)) return GDN_ERR_NULL_POINTER;
     if (ck_bytes > 0 && !h_ckpt) return GDN_ERR_NULL_POINTER;
-    const void* ptrs[] = {q, k, v, log_g, beta, h0, hT, o, workspace, h_ckpt, A_log, dt_bias};
+    const void* ptrs[] = {q, k, v, log_g, beta, h0, hT, o, workspace, h_ckpt, A_log, dt_bias, cu};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
 
@@ -141,7 +145,8 @@ gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, cons
     const Range ins[] = {range_of(q, BT ? qk_bytes : 0), range_of(k, BT ? qk_bytes : 0),
                          range_of(v, BT ? v_bytes : 0), range_of(log_g, BT ? g_bytes : 0),
                          range_of(beta, BT ? g_bytes : 0), range_of(A_log, A_log ? par_bytes : 0),
-                         range_of(dt_bias, dt_bias ? par_bytes : 0)};
+                         range_of(dt_bias, dt_bias ? par_bytes : 0),
+                         range_of(cu, cu ? ((size_t)p->B + 1) * sizeof(int32_t) : 0)};
     const Range r_o = range_of(o, BT ? v_bytes : 0);
     const Range r_hT = range_of(hT, hT ? s_bytes : 0);
     const Range r_h0 = range_of(h0, h0 ? s_bytes : 0);
@@ -160,11 +165,13 @@ gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, cons
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (p->B == 0 || p->Hv == 0) return GDN_OK;
     hipError_t err;
-    if (p->T == 0) {
+    if (p->T == 0 || BT == 0) {   // every sequence is empty
         err = gdn::launch_state_copy(h0, hT, s_bytes / sizeof(float), stream);
         return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
     }
     gdn::PrefillArgs a = prefill_args(p);
+    a.cu = cu;
+    a.total = total;
     a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
     a.A_log = A_log; a.dt_bias = dt_bias;
     a.h0 = h0; a.hT = hT; a.o = o; a.ws = workspace; a.ws_bytes = workspace_bytes;
@@ -214,6 +221,21 @@ gdn_status gdn_chunk_prefill_gated(const gdn_problem* p, const void* q, const vo
     if (ckpt_every == 0 && h_ckpt) return GDN_ERR_BAD_SHAPE;
     return prefill_impl(p, q, k, v, a, b, A_log, dt_bias, h0, hT, o, h_ckpt, ckpt_every,
                         workspace, workspace_bytes, hip_stream);
+}
+
+gdn_status gdn_chunk_prefill_varlen(const gdn_problem* p, const int32_t* cu_seqlens,
+                                    int64_t total_tokens, const void* q, const void* k,
+                                    const void* v, const float* log_g, const float* beta,
+                                    const float* h0, float* hT, void* o, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream) {
+    const gdn_status st = check_problem(p, false);
+    if (st != GDN_OK) return st;
+    if (total_tokens < 0) return GDN_ERR_BAD_SHAPE;
+    const long long elems = (long long)total_tokens * p->Hv * p->dv;
+    if (total_tokens > 0x7fffffffLL || elems > (1LL << 46)) return GDN_ERR_BAD_SHAPE;
+    if (p->B > 0 && !cu_seqlens) return GDN_ERR_NULL_POINTER;
+    return prefill_impl(p, q, k, v, log_g, beta, nullptr, nullptr, h0, hT, o, nullptr, 0,
+                        workspace, workspace_bytes, hip_stream, cu_seqlens, total_tokens);
 }
 
 }  // extern "C"

@@ -46,6 +46,24 @@ __device__ __forceinline__ float raw_log_decay(float a, float A_log, float dt_bi
 }
 __device__ __forceinline__ float raw_beta(float b) { return 1.0f / (1.0f + expf(-b)); }
 
+// Tokens of sequence b on the token axis: [first, first + count).  Without
+// cu_seqlens sequence b is tokens [b T, b T + T).  With them (packed
+// variable-length batch) the bounds are clamped into [0, total] and the count
+// to T, the longest sequence the launch was sized for, so any cu_seqlens
+// content keeps every access in bounds.
+__device__ __forceinline__ void seq_span(const int* cu, int b, int T, long long total,
+                                         size_t& first, int& count) {
+    if (!cu) {
+        first = (size_t)b * T;
+        count = T;
+        return;
+    }
+    const long long s0 = min(max((long long)cu[b], 0LL), total);
+    const long long s1 = min(max((long long)cu[b + 1], s0), total);
+    first = (size_t)s0;
+    count = (int)min(s1 - s0, (long long)T);
+}
+
 // 1 / max(sqrt(ss), 1e-6): the L2-normalisation factor used by every kernel.
 __device__ __forceinline__ float inv_l2(float ss) {
     return 1.0f / fmaxf(sqrtf(ss), 1e-6f);

@@ -36,6 +36,8 @@ struct PrefillArgs {
     float* ckpt;       // [B, nck, Hv, D, D] state checkpoints, or null
     int ckpt_every;    // tokens between checkpoints (a multiple of C), 0 if none
     int nck;           // ceil(T / ckpt_every), 0 if none
+    const int* cu;     // device [B + 1] sequence starts on a packed token axis, or null
+    long long total;   // tokens on the token axis (B * T without cu)
 };
 
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);

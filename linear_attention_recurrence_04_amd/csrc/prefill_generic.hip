@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(
     const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     const float* h0, float* hT, TIn* __restrict__ o,
     int T, int Hk, int Hv, int l2norm, float q_scale,
-    float* __restrict__ ckpt, int ckpt_every, int nck) {
+    float* __restrict__ ckpt, int ckpt_every, int nck, const int* __restrict__ cu, long long total) {
     constexpr int NT = 256;
     constexpr int TPR = NT / C;   // threads per chunk row (normalisation)
     constexpr int P = NT / BV;    // partial-sum lanes per column (solve)
@@ -58,20 +58,23 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(
     const int hk = h / (Hv / Hk);
     const int j0 = blockIdx.y * BV;
     const size_t state_base = (size_t)bh * D * D;
+    size_t tb0;   // first token of sequence b
+    int Tb;       // its length (T for equal-length batches)
+    seq_span(cu, b, T, total, tb0, Tb);
 
     for (int e = tid; e < D * BV; e += NT) {
         const int i = e / BV, j = e % BV;
         Ss[i][j] = h0 ? h0[state_base + (size_t)i * D + j0 + j] : 0.f;
     }
 
-    for (int t0 = 0; t0 < T; t0 += C) {
-        const int L = min(C, T - t0);
+    for (int t0 = 0; t0 < Tb; t0 += C) {
+        const int L = min(C, Tb - t0);
         __syncthreads();  // previous chunk fully consumed
         for (int e = tid; e < C * D; e += NT) {
             const int r = e / D, i = e % D;
             float kv = 0.f, qv = 0.f;
             if (r < L) {
-                const size_t off = (((size_t)b * T + t0 + r) * Hk + hk) * D + i;
+                const size_t off = ((tb0 + t0 + r) * Hk + hk) * D + i;
                 kv = to_f32(k[off]);
                 qv = to_f32(q[off]);
             }
@@ -80,11 +83,11 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(
         }
         for (int e = tid; e < C * BV; e += NT) {
             const int r = e / BV, j = e % BV;
-            Xs[r][j] = (r < L) ? to_f32(v[(((size_t)b * T + t0 + r) * Hv + h) * D + j0 + j]) : 0.f;
+            Xs[r][j] = (r < L) ? to_f32(v[((tb0 + t0 + r) * Hv + h) * D + j0 + j]) : 0.f;
         }
         if (tid < C) {
             const bool in = tid < L;
-            const size_t gi = ((size_t)b * T + t0 + tid) * Hv + h;
+            const size_t gi = (tb0 + t0 + tid) * Hv + h;
             float lgv = in ? log_g[gi] : 0.f, btv = in ? beta[gi] : 0.f;
             if (A_log && in) {   // raw projections a, b
                 lgv = raw_log_decay(lgv, A_log[h], dt_bias[h]);
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(
                 for (int i = 0; i < D; ++i) acc += Qs[r][i] * Ss[i][j];
                 acc *= Gm[r];
                 for (int s = 0; s <= r; ++s) acc += Mm[r][s] * Xs[s][j];
-                o[(((size_t)b * T + t0 + r) * Hv + h) * D + j0 + j] = from_f32<TIn>(q_scale * acc);
+                o[((tb0 + t0 + r) * Hv + h) * D + j0 + j] = from_f32<TIn>(q_scale * acc);
             }
         }
         __syncthreads();
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(
         const float GL = Gm[C - 1];
         const int done = t0 + L;
         float* ck = nullptr;
-        if (ckpt && (done % ckpt_every == 0 || done == T))
+        if (ckpt && (done % ckpt_every == 0 || done == Tb))
             ck = ckpt + (((size_t)b * nck + (done + ckpt_every - 1) / ckpt_every - 1) * Hv + h) * D * D;
         for (int e = tid; e < D * BV; e += NT) {
             const int i = e / BV, j = e % BV;
@@ -207,7 +210,7 @@ static hipError_t launch_generic(const PrefillArgs& a, hipStream_t stream) {
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.v), a.log_g, a.beta, a.A_log, a.dt_bias, a.h0, a.hT,
                        static_cast<TIn*>(a.o), a.T, a.Hk, a.Hv, a.l2norm, a.q_scale,
-                       a.ckpt, a.ckpt_every, a.nck);
+                       a.ckpt, a.ckpt_every, a.nck, a.cu, a.total);
     return hipGetLastError();
 }
 

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const unsigned char* __restrict__ ws, const float* h0, float* hT, bf16_t* __restrict__ o,
     int T, int NTc, int Hk, int Hv, float q_scale, int xcd_remap,
-    float* __restrict__ ckpt, int ckpt_every, int nck) {
+    float* __restrict__ ckpt, int ckpt_every, int nck, const int* __restrict__ cu, long long total) {
     __shared__ ScanSmem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -140,12 +140,16 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     const int b = bh / Hv;
     const int h = bh - b * Hv;
     const int hk = h / (Hv / Hk);
+    size_t tb0;   // first token of sequence b
+    int Tb;       // its length (T for equal-length batches)
+    seq_span(cu, b, T, total, tb0, Tb);
+    const int NTb = (Tb + C - 1) / C;    // its chunks (records are laid out for NTc)
     const size_t state_base = (size_t)bh * D * D;
     const unsigned char* rec0 = ws + (size_t)bh * NTc * WS_REC;
-    const bf16_t* kbase = k + ((size_t)b * T * Hk + hk) * D;
-    const bf16_t* qbase = q + ((size_t)b * T * Hk + hk) * D;
-    const bf16_t* vbase = v + ((size_t)b * T * Hv + h) * D + j0;
-    bf16_t* obase = o + ((size_t)b * T * Hv + h) * D + j0;
+    const bf16_t* kbase = k + (tb0 * Hk + hk) * D;
+    const bf16_t* qbase = q + (tb0 * Hk + hk) * D;
+    const bf16_t* vbase = v + (tb0 * Hv + h) * D + j0;
+    bf16_t* obase = o + (tb0 * Hv + h) * D + j0;
     const int rowk = Hk * D;             // element stride between tokens of q and k
     const int rowv = Hv * D;             // element stride between tokens of v and o
 
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 offv[u] = 2u * (uint32_t)(min(s2, last) * rowv + 8 * ((lane & 3) ^ ((s2 >> 2) & 3)));
             }
         };
-        const int last_rows = T - (NTc - 1) * C - 1;   // last row of the last chunk
+        const int last_rows = Tb - (NTb - 1) * C - 1;   // last row of the last chunk
         kq_offsets(offk, C - 1);
         kq_offsets(offq, C - 1);
         v_offsets(C - 1);
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
         // block), so that one wait count fits every wave.
         constexpr int NKLOADS = 7;
         auto load_k = [&](int chunk, int slot) __attribute__((always_inline)) {
-            if (chunk == NTc - 1) {   // the last chunk: clamp its rows
+            if (chunk == NTb - 1) {   // the last chunk: clamp its rows
                 kq_offsets(offk, last_rows);
                 v_offsets(last_rows);
             }
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
             if (lw == 3) lds_load16(kc + offk[NKB - 1], &B.K[64 * (lw + LWAVES * (NKB - 1))]);   // count filler
         };
         auto load_q = [&](int chunk, int slot) __attribute__((always_inline)) {
-            if (chunk == NTc - 1) kq_offsets(offq, last_rows);
+            if (chunk == NTb - 1) kq_offsets(offq, last_rows);
             QSet& B = sm.qs[slot];
             const int t0 = chunk * C;
             const unsigned char* qc = reinterpret_cast<const unsigned char*>(qbase + (size_t)t0 * rowk);
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
         else toucher = first_block && (h % (Hv / Hk)) == 0;
         auto touch = [&](int chunk) __attribute__((always_inline)) {
             const int t0 = chunk * C;
-            const int row = t0 + min(lane, T - t0 - 1);
+            const int row = t0 + min(lane, Tb - t0 - 1);
             uint32_t* sink = sm.sink[lw];
             const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;   // 106 lines of 128 bytes
             if (lw == 0) {
@@ -258,20 +262,20 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
         // outstanding covers the q side of chunk c and the k side of chunk
         // c + 1 (issued an iteration ago): what the next iteration reads.
         if (toucher)
-            for (int c = 1; c <= TOUCH_AHEAD && c < NTc; ++c) touch(c);
-        load_k(0, 0);
-        if (NTc > 1) load_k(1, 1);
+            for (int c = 1; c <= TOUCH_AHEAD && c < NTb; ++c) touch(c);
+        if (NTb > 0) load_k(0, 0);
+        if (NTb > 1) load_k(1, 1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        for (int c = 0; c <= NTc; ++c) {
-            if (c < NTc) load_q(c, c & 1);
+        for (int c = 0; c <= NTb; ++c) {
+            if (c < NTb) load_q(c, c & 1);
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            const bool kload = c + 2 < NTc;
+            const bool kload = c + 2 < NTb;
             if (kload) load_k(c + 2, (c + 2) % 3);
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            const bool tload = toucher && c + TOUCH_AHEAD < NTc;
+            const bool tload = toucher && c + TOUCH_AHEAD < NTb;
             if (tload) touch(c + TOUCH_AHEAD);
             if (kload && tload) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NKLOADS + NTOUCH));
             else if (kload) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NKLOADS));
@@ -307,8 +311,8 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
 #pragma unroll
             for (int a = 0; a < 8; ++a) S[a] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        for (int c = 0; c <= NTc; ++c) {
-            if (c < NTc) {
+        for (int c = 0; c <= NTb; ++c) {
+            if (c < NTb) {
                 const KSet& B = sm.ks[c % 3];
                 // ---- K operands of the first k step, then the bf16 state
                 //      operands (also left in LDS for the output wave)
@@ -420,8 +424,8 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 // ---- checkpoint slot: the state after every ckpt_every tokens
                 //      and after the last token
                 if (ckpt) {
-                    const int done = min((c + 1) * C, T);
-                    if (done % ckpt_every == 0 || c == NTc - 1) {
+                    const int done = min((c + 1) * C, Tb);
+                    if (done % ckpt_every == 0 || c == NTb - 1) {
                         const int slot = (done + ckpt_every - 1) / ckpt_every - 1;
                         float* cp = ckpt + (((size_t)b * nck + slot) * Hv + h) * D * D + jw + n;
 #pragma unroll
@@ -444,7 +448,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     }
 
     // ======================= output waves =======================
-    for (int c = 0; c <= NTc; ++c) {
+    for (int c = 0; c <= NTb; ++c) {
         if (c >= 1) {
             const int cc = c - 1;
             const QSet& B = sm.qs[cc & 1];
@@ -500,7 +504,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
             // ---- the strip's 64 rows x 32 bytes back from LDS (this wave's own
             //      writes, so no barrier) and to HBM in 16-byte pieces
             const int t0 = cc * C;
-            const int L = min(C, T - t0);
+            const int L = min(C, Tb - t0);
             bf16_t* oc = obase + (size_t)t0 * rowv + SW * strip;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -539,7 +543,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
     } else {
         hipLaunchKernelGGL(chunk_prep_kernel, dim3(prep_blocks), dim3(NT), 0, stream,
                            static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k), a.log_g,
-                           a.beta, nullptr, nullptr, ws, a.T, NTc, a.Hk, a.Hv, a.l2norm);
+                           a.beta, nullptr, nullptr, ws, a.T, NTc, a.Hk, a.Hv, a.l2norm, a.cu,
+                           a.total);
         err = hipGetLastError();
     }
     if (err != hipSuccess) return err;
@@ -549,7 +554,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
                        static_cast<const bf16_t*>(a.v), ws, a.h0, a.hT,
                        static_cast<bf16_t*>(a.o), a.T, NTc, a.Hk, a.Hv, a.q_scale, remap,
-                       a.ckpt, a.ckpt_every, a.nck);
+                       a.ckpt, a.ckpt_every, a.nck, a.cu, a.total);
     return hipGetLastError();
 }
 

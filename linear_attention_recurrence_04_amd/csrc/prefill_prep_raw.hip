@@ -20,7 +20,8 @@ hipError_t launch_prep_raw(const PrefillArgs& a, int NTc, unsigned char* ws, hip
     const int blocks = a.B * a.Hk * NTc;
     hipLaunchKernelGGL(chunk_prep_raw_kernel, dim3(blocks), dim3(NT), 0, stream,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k), a.log_g,
-                       a.beta, a.A_log, a.dt_bias, ws, a.T, NTc, a.Hk, a.Hv, a.l2norm);
+                       a.beta, a.A_log, a.dt_bias, ws, a.T, NTc, a.Hk, a.Hv, a.l2norm, a.cu,
+                       a.total);
     return hipGetLastError();
 }
 

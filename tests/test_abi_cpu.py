@@ -175,3 +175,21 @@ def test_multi_token_decode_rejects_bad_arguments():
     assert decode_multi(P(T=4, dk=32, dv=32)) == 3
     # the chunk field is ignored by decode
     assert decode_multi(P(T=4, chunk=48), st=None) == 1
+
+
+def prefill_varlen(prob, cu=fake(11), total=300, q=fake(0), o=fake(7), hT=fake(6), h0=None):
+    return B.lib().gdn_chunk_prefill_varlen(ctypes.byref(prob), cu, total, q, fake(1), fake(2),
+                                            fake(3), fake(4), h0, hT, o, None, 0, None)
+
+
+def test_varlen_prefill_rejects_bad_arguments():
+    assert prefill_varlen(P(B=3, T=128), total=-1) == 2
+    assert prefill_varlen(P(B=3, T=128), total=1 << 31) == 2
+    assert prefill_varlen(P(B=3, T=128), cu=None) == 1
+    assert prefill_varlen(P(B=3, T=128), cu=fake(11, 4)) == 4
+    assert prefill_varlen(P(B=3, T=128), cu=fake(7, 64)) == 7     # offsets inside o
+    assert prefill_varlen(P(B=3, T=128), q=None) == 1
+    assert prefill_varlen(P(B=3, T=128, Hv=3)) == 2
+    # o sized by total_tokens: an hT just past a 300-token o does not overlap it,
+    # one starting inside it does (2 heads x 64 x 4 bytes per token)
+    assert prefill_varlen(P(B=3, T=128), hT=fake(7, 300 * 2 * 64 * 4 - 16)) == 7
