@@ -196,6 +196,80 @@ def bench_prefill_varlen(torch, gdn, p, steps, warmup):
     return time_stream(torch, call, steps) / steps
 
 
+def measured_peaks(torch):
+    """Achievable figures on this GPU, for fractions against measured as well as
+    published peaks: a 2 GiB device copy (read + write) and a large bf16 GEMM
+    (hipBLASLt through torch)."""
+    n = 512 * 1024 * 1024                      # fp32 elements = 2 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ms = time_stream(torch, lambda: dst.copy_(src), 10) / 10
+    copy_gbps = 2 * n * 4 / (ms * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    c = a @ b
+    ms = time_stream(torch, lambda: torch.matmul(a, b, out=c), 10) / 10
+    gemm_tflops = 2 * m ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": round(copy_gbps, 1), "bf16_gemm_8192_TFLOPs": round(gemm_tflops, 1),
+            "note": "2 GiB device copy (bytes read + written); 8192^3 bf16 torch.matmul"}
+
+
+def gpu_state():
+    """Clock and power readings from rocm-smi, when the tool is present (read only)."""
+    import shutil
+    import subprocess
+    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe, "-d", "0", "--showclocks", "--showpower", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip() else None
+    except (OSError, ValueError, subprocess.TimeoutExpired):
+        return None
+    if not isinstance(data, dict):
+        return None
+    card = next(iter(data.values()), {})
+    return {k: v for k, v in card.items() if isinstance(v, str) and len(v) < 64}
+
+
+def bench_decode_graph(torch, gdn, d, steps, warmup, chunk_steps: int = 100):
+    """ms per decode step when the steps are replayed from captured HIP graphs:
+    `chunk_steps` consecutive steps (fixed input pointers) per graph, replayed
+    until `steps` steps have run."""
+    st = gi.make_decode_steps(d, 0, steps=chunk_steps)
+    dv = {n: torch.from_numpy(st[n]).cuda() for n in st}
+    for n in ("q", "k", "v"):
+        dv[n] = dv[n].to(torch.bfloat16)
+    state = torch.from_numpy(gi.make_decode_state(d, 0)).cuda()
+    out = torch.empty((d.B, d.Hv, d.dv), dtype=torch.bfloat16, device="cuda")
+
+    def steps_fn():
+        for s in range(chunk_steps):
+            gdn.gdn_decode_step(dv["q"][s], dv["k"][s], dv["v"][s], dv["log_g"][s], dv["beta"][s],
+                                state, out=out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            steps_fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps_fn()
+    torch.cuda.synchronize()
+    reps = max(steps // chunk_steps, 1)
+    log(f"decode from HIP graphs: timing {reps} x {chunk_steps} steps")
+    ms = time_stream(torch, graph.replay, reps)
+    return ms / (reps * chunk_steps)
+
+
 def bench_decode(torch, gdn, d, steps, warmup):
     log(f"decode workload {d.name}: generating {steps} steps of inputs")
     st = gi.make_decode_steps(d, 0, steps=steps)
@@ -255,11 +329,11 @@ def bench_decode_multi(torch, gdn, d, steps, warmup, tokens_per_call: int):
     return ms / calls, calls
 
 
-def cpu_baseline(p, sample_tokens: int):
+def cpu_baseline(p, sample_tokens: int, cores=None):
     """The oracle as it stands, on the first `sample_tokens` tokens of the
     prefill workload (all heads), threaded over (b, h) on the host cores."""
     import oracle
-    cores = max(1, min(os.cpu_count() or 1, 64))
+    cores = cores or max(1, min(os.cpu_count() or 1, 64))
     inp = gi.make_prefill(p, 0, T=sample_tokens)
     t0 = time.perf_counter()
     oracle.gdn_sequential(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["beta"], inp["h0"],
@@ -420,10 +494,42 @@ def main():
         }
         log(f"decode, {Tm} tokens per call: {ms_m * 1e3:.2f} us/call, "
             f"{result['decode_multi']['tokens_per_s']:.0f} tok/s")
+        # the same steps replayed from captured HIP graphs (no per-step launch cost)
+        ms_gr = bench_decode_graph(torch, gdn, d, args.decode_steps, min(args.warmup, 10) or 1)
+        result["decode_graph"] = {"us_per_step": round(ms_gr * 1e3, 3),
+                                  "state_update_GBps": round(nb / (ms_gr * 1e-3) / 1e9, 2),
+                                  "vs_stream_launches": round(ms_d / ms_gr, 3)}
+        log(f"decode from HIP graphs: {ms_gr * 1e3:.2f} us/step")
+        # twice the batch: 402.7 MB of state, more than the 256 MB Infinity Cache
+        d2 = gi.DecodeProblem(d.name.replace("B64", "B128"), 2 * d.B, d.Hk, d.Hv, d.dk, d.dv, 200)
+        ms_2 = bench_decode(torch, gdn, d2, d2.steps, min(args.warmup, 10) or 1)
+        nb2 = decode_bytes(d2)
+        result["decode_B128"] = {"workload": d2.name, "steps": d2.steps,
+                                 "us_per_step": round(ms_2 * 1e3, 3),
+                                 "state_update_GBps": round(nb2 / (ms_2 * 1e-3) / 1e9, 2),
+                                 "frac_of_hbm_peak": round(nb2 / (ms_2 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 5)}
+        log(f"decode B=128: {ms_2 * 1e3:.2f} us/step, {result['decode_B128']['state_update_GBps']:.1f} GB/s")
+
+    if args.only == "all" and not args.no_extras:
+        peaks = measured_peaks(torch)
+        result["measured_peaks"] = peaks
+        if "roofline" in result:
+            r = result["roofline"]
+            r["frac_of_measured_peak"] = round(
+                r["achieved"] / (peaks["hbm_copy_GBps"] if r["unit"] == "GB/s" else peaks["bf16_gemm_8192_TFLOPs"]), 5)
+            r["compute"]["frac_of_measured_bf16_gemm"] = round(
+                r["compute"]["achieved_tflops"] / peaks["bf16_gemm_8192_TFLOPs"], 5)
+        if "decode" in result:
+            dr = result["decode"]["roofline"]
+            dr["frac_of_measured_peak"] = round(dr["achieved"] / peaks["hbm_copy_GBps"], 5)
+        result["gpu_state"] = gpu_state()
 
     if not args.no_cpu_baseline and args.only in ("all", "prefill"):
         log("cpu baseline: oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(p, args.cpu_sample_tokens)
+        if not args.no_extras:
+            log("cpu baseline: one thread, 512 tokens")
+            result["cpu_baseline_1thread"] = cpu_baseline(p, 512, cores=1)
 
     print(json.dumps(result), flush=True)
 
