@@ -334,6 +334,21 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 s16x4 vt[4];
                 f32x4 btv[4], grk[4];
                 bf16x8 at0[4], at1[2];   // T operands
+                f32x4 wg[4];             // exp(gamma_C - gamma) rk of the four row tiles
+                float GC;                // Gamma_C
+                // k^T operands of the state update, read transposed from the k
+                // rows: tile a, k step kk; lane (g, n) gets k column lpos(16a + n)
+                // at tokens 32kk + 4g + j and 32kk + 16 + 4g + j
+                const unsigned char* Kb = reinterpret_cast<const unsigned char*>(B.K);
+                auto ldkt = [&](int a, int kk) __attribute__((always_inline)) {
+                    const int r0 = 32 * kk + 4 * g + (n >> 2);
+                    const int ch = 4 * (a >> 1) + (n & 3);
+                    const int sz = ((n >> 2) << 2) | g;     // swz(r0) = swz(r0 + 16)
+                    const s16x4 lo = ld_tr4(Kb + r0 * 256 + 16 * (ch ^ sz) + 8 * (a & 1));
+                    const s16x4 hi = ld_tr4(Kb + (r0 + 16) * 256 + 16 * (ch ^ sz) + 8 * (a & 1));
+                    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                };
+                bf16x8 akt[8][2];
                 const unsigned char* Vb = reinterpret_cast<const unsigned char*>(B.V);
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
@@ -364,6 +379,15 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                     if (ks == 3) {
                         at1[0] = __builtin_bit_cast(bf16x8, B.T[imgq(32 + n, 4 + g)]);
                         at1[1] = __builtin_bit_cast(bf16x8, B.T[imgq(48 + n, 4 + g)]);
+                        wg[0] = *reinterpret_cast<const f32x4*>(&B.gate[C + 4 * g]);
+                        wg[1] = *reinterpret_cast<const f32x4*>(&B.gate[C + 16 + 4 * g]);
+                        wg[2] = *reinterpret_cast<const f32x4*>(&B.gate[C + 32 + 4 * g]);
+                        wg[3] = *reinterpret_cast<const f32x4*>(&B.gate[C + 48 + 4 * g]);
+                        GC = B.gate[3 * C];
+                    }
+                    if (ks == 3) {
+#pragma unroll
+                        for (int a = 0; a < 8; ++a) akt[a][0] = ldkt(a, 0);
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -383,27 +407,6 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                         X[i][t] = btv[i][t] * (__uint_as_float((uint32_t)(uint16_t)vt[i][t] << 16) - grk[i][t] * KS[i][t]);
                 const bf16x8 XB0 = pack8(X[0], X[1]);
                 const bf16x8 XB1 = pack8(X[2], X[3]);
-                // ---- k^T operands of the state update, read transposed from the
-                //      k rows: tile a, k step kk; lane (g, n) gets k column
-                //      lpos(16a + n) at tokens 32kk + 4g + j and 32kk + 16 + 4g + j
-                const unsigned char* Kb = reinterpret_cast<const unsigned char*>(B.K);
-                bf16x8 akt[8][2];
-#pragma unroll
-                for (int a = 0; a < 8; ++a)
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const int r0 = 32 * kk + 4 * g + (n >> 2);
-                        const int ch = 4 * (a >> 1) + (n & 3);
-                        const int sz = ((n >> 2) << 2) | g;     // swz(r0) = swz(r0 + 16)
-                        const s16x4 lo = ld_tr4(Kb + r0 * 256 + 16 * (ch ^ sz) + 8 * (a & 1));
-                        const s16x4 hi = ld_tr4(Kb + (r0 + 16) * 256 + 16 * (ch ^ sz) + 8 * (a & 1));
-                        akt[a][kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    }
-                const f32x4 wlo0 = *reinterpret_cast<const f32x4*>(&B.gate[C + 4 * g]);
-                const f32x4 whi0 = *reinterpret_cast<const f32x4*>(&B.gate[C + 16 + 4 * g]);
-                const f32x4 wlo1 = *reinterpret_cast<const f32x4*>(&B.gate[C + 32 + 4 * g]);
-                const f32x4 whi1 = *reinterpret_cast<const f32x4*>(&B.gate[C + 48 + 4 * g]);
-                const float GC = B.gate[3 * C];
                 __builtin_amdgcn_sched_barrier(0);
                 // ---- Delta = T X (T lower triangular: row tile i needs k steps <= i/2)
                 f32x4 Dl[4];
@@ -411,11 +414,15 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 for (int i = 0; i < 4; ++i) Dl[i] = mfma32(at0[i], XB0, f32x4{0.f, 0.f, 0.f, 0.f});
                 Dl[2] = mfma32(at1[0], XB1, Dl[2]);
                 Dl[3] = mfma32(at1[1], XB1, Dl[3]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int a = 0; a < 8; ++a) akt[a][1] = ldkt(a, 1);
+                __builtin_amdgcn_sched_barrier(0);
                 // ---- Delta operands: plain (to the output wave) and scaled (state update)
                 sm.Dx[c & 1][strip][0][lane] = pack8(Dl[0], Dl[1]);
                 sm.Dx[c & 1][strip][1][lane] = pack8(Dl[2], Dl[3]);
-                const bf16x8 DWB0 = pack8(Dl[0] * wlo0, Dl[1] * whi0);
-                const bf16x8 DWB1 = pack8(Dl[2] * wlo1, Dl[3] * whi1);
+                const bf16x8 DWB0 = pack8(Dl[0] * wg[0], Dl[1] * wg[1]);
+                const bf16x8 DWB1 = pack8(Dl[2] * wg[2], Dl[3] * wg[3]);
                 // ---- state update S <- Gamma_C S + K^T (wrk Delta), 8 independent tiles
 #pragma unroll
                 for (int a = 0; a < 8; ++a) S[a] = mfma32(akt[a][0], DWB0, S[a] * GC);
