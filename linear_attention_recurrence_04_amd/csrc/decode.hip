@@ -63,107 +63,107 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
     const int NTOK = MULTI ? T : 1;   // a single step compiles to straight-line code
     for (int t = 0; t < NTOK; ++t) {
-    if (t > 0) __syncthreads();   // the previous token is done with kh, qh, dl
-    const size_t bt_idx = (size_t)b * T + t;   // (sequence, token)
-    const size_t row = bt_idx * Hv + h;        // (sequence, token, value head)
+        if (t > 0) __syncthreads();   // the previous token is done with kh, qh, dl
+        const size_t bt_idx = (size_t)b * T + t;   // (sequence, token)
+        const size_t row = bt_idx * Hv + h;        // (sequence, token, value head)
 
-    // 2. q, k of the key head, normalised in fp32
-    float kv = 0.f, qv = 0.f;
-    if (tid < D) {
-        const size_t off = (bt_idx * Hk + hk) * D + tid;
-        kv = to_f32(k[off]);
-        qv = to_f32(q[off]);
-    }
-    float ssk = group_sum<64>(kv * kv);
-    float ssq = group_sum<64>(qv * qv);
-    if ((tid & 63) == 0) {
-        wsum[tid >> 6][0] = ssk;
-        wsum[tid >> 6][1] = ssq;
-    }
-    __syncthreads();
-    float rk = 1.f, rq = 1.f;
-    if (l2norm) {
-        float tk = 0.f, tq = 0.f;
-#pragma unroll
-        for (int w = 0; w < (D + 63) / 64; ++w) {
-            tk += wsum[w][0];
-            tq += wsum[w][1];
+        // 2. q, k of the key head, normalised in fp32
+        float kv = 0.f, qv = 0.f;
+        if (tid < D) {
+            const size_t off = (bt_idx * Hk + hk) * D + tid;
+            kv = to_f32(k[off]);
+            qv = to_f32(q[off]);
         }
-        rk = inv_l2(tk);
-        rq = inv_l2(tq);
-    }
-    if (tid < D) {
-        kh[tid] = kv * rk;
-        qh[tid] = qv * rq;
-    }
-    __syncthreads();
-    // k_hat . q_hat (needed by the fused output identity)
-    float kq_part = (tid < D) ? kh[tid] * qh[tid] : 0.f;
-    kq_part = group_sum<64>(kq_part);
-    if ((tid & 63) == 0) wsum[tid >> 6][2] = kq_part;
-
-    // 3. per-thread partial reads a = S^T k, c = S^T q over its rows
-    float pa[4] = {0.f, 0.f, 0.f, 0.f}, pc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const float kr = kh[rg + RG * i];
-        const float qr = qh[rg + RG * i];
-        pa[0] += s[i].x * kr; pa[1] += s[i].y * kr; pa[2] += s[i].z * kr; pa[3] += s[i].w * kr;
-        pc[0] += s[i].x * qr; pc[1] += s[i].y * qr; pc[2] += s[i].z * qr; pc[3] += s[i].w * qr;
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        red[0][rg][4 * cg + c] = pa[c];
-        red[1][rg][4 * cg + c] = pc[c];
-    }
-    __syncthreads();
-
-    // 4. column totals, delta and the output (one thread per column)
-    float lgv = log_g[row], bt = beta[row];
-    if (A_log) {   // raw projections a, b
-        const int h = bh % Hv;
-        lgv = raw_log_decay(lgv, A_log[h], dt_bias[h]);
-        bt = raw_beta(bt);
-    }
-    const float g = expf(lgv);
-    if (tid < D) {
-        float a = 0.f, c = 0.f;
-#pragma unroll
-        for (int r = 0; r < RG; ++r) {
-            a += red[0][r][tid];
-            c += red[1][r][tid];
+        float ssk = group_sum<64>(kv * kv);
+        float ssq = group_sum<64>(qv * qv);
+        if ((tid & 63) == 0) {
+            wsum[tid >> 6][0] = ssk;
+            wsum[tid >> 6][1] = ssq;
         }
-        float kq = 0.f;
-#pragma unroll
-        for (int w = 0; w < (D + 63) / 64; ++w) kq += wsum[w][2];
-        const float vj = to_f32(v[row * D + tid]);
-        const float delta = bt * (vj - g * a);
-        dl[tid] = delta;
-        o[row * D + tid] = from_f32<TIn>(q_scale * (g * c + delta * kq));
-    }
-    __syncthreads();
+        __syncthreads();
+        float rk = 1.f, rq = 1.f;
+        if (l2norm) {
+            float tk = 0.f, tq = 0.f;
+    #pragma unroll
+            for (int w = 0; w < (D + 63) / 64; ++w) {
+                tk += wsum[w][0];
+                tq += wsum[w][1];
+            }
+            rk = inv_l2(tk);
+            rq = inv_l2(tq);
+        }
+        if (tid < D) {
+            kh[tid] = kv * rk;
+            qh[tid] = qv * rq;
+        }
+        __syncthreads();
+        // k_hat . q_hat (needed by the fused output identity)
+        float kq_part = (tid < D) ? kh[tid] * qh[tid] : 0.f;
+        kq_part = group_sum<64>(kq_part);
+        if ((tid & 63) == 0) wsum[tid >> 6][2] = kq_part;
 
-    // 5. S <- g S + k delta^T (and the per-token state when asked for)
-    const float4 d4 = *reinterpret_cast<const float4*>(&dl[4 * cg]);
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const float kr = kh[rg + RG * i];
-        float4 n;
-        n.x = g * s[i].x + kr * d4.x;
-        n.y = g * s[i].y + kr * d4.y;
-        n.z = g * s[i].z + kr * d4.z;
-        n.w = g * s[i].w + kr * d4.w;
-        if (MULTI)
-            s[i] = n;
-        else   // a single step writes back over the same addresses at once
-            *reinterpret_cast<float4*>(S + (size_t)(rg + RG * i) * D + 4 * cg) = n;
-    }
-    if (MULTI && states) {
-        float* St = states + row * D * D;
-#pragma unroll
-        for (int i = 0; i < RPT; ++i)
-            *reinterpret_cast<float4*>(St + (size_t)(rg + RG * i) * D + 4 * cg) = s[i];
-    }
+        // 3. per-thread partial reads a = S^T k, c = S^T q over its rows
+        float pa[4] = {0.f, 0.f, 0.f, 0.f}, pc[4] = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float kr = kh[rg + RG * i];
+            const float qr = qh[rg + RG * i];
+            pa[0] += s[i].x * kr; pa[1] += s[i].y * kr; pa[2] += s[i].z * kr; pa[3] += s[i].w * kr;
+            pc[0] += s[i].x * qr; pc[1] += s[i].y * qr; pc[2] += s[i].z * qr; pc[3] += s[i].w * qr;
+        }
+    #pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            red[0][rg][4 * cg + c] = pa[c];
+            red[1][rg][4 * cg + c] = pc[c];
+        }
+        __syncthreads();
+
+        // 4. column totals, delta and the output (one thread per column)
+        float lgv = log_g[row], bt = beta[row];
+        if (A_log) {   // raw projections a, b
+            const int h = bh % Hv;
+            lgv = raw_log_decay(lgv, A_log[h], dt_bias[h]);
+            bt = raw_beta(bt);
+        }
+        const float g = expf(lgv);
+        if (tid < D) {
+            float a = 0.f, c = 0.f;
+    #pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                a += red[0][r][tid];
+                c += red[1][r][tid];
+            }
+            float kq = 0.f;
+    #pragma unroll
+            for (int w = 0; w < (D + 63) / 64; ++w) kq += wsum[w][2];
+            const float vj = to_f32(v[row * D + tid]);
+            const float delta = bt * (vj - g * a);
+            dl[tid] = delta;
+            o[row * D + tid] = from_f32<TIn>(q_scale * (g * c + delta * kq));
+        }
+        __syncthreads();
+
+        // 5. S <- g S + k delta^T (and the per-token state when asked for)
+        const float4 d4 = *reinterpret_cast<const float4*>(&dl[4 * cg]);
+    #pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float kr = kh[rg + RG * i];
+            float4 n;
+            n.x = g * s[i].x + kr * d4.x;
+            n.y = g * s[i].y + kr * d4.y;
+            n.z = g * s[i].z + kr * d4.z;
+            n.w = g * s[i].w + kr * d4.w;
+            if (MULTI)
+                s[i] = n;
+            else   // a single step writes back over the same addresses at once
+                *reinterpret_cast<float4*>(S + (size_t)(rg + RG * i) * D + 4 * cg) = n;
+        }
+        if (MULTI && states) {
+            float* St = states + row * D * D;
+    #pragma unroll
+            for (int i = 0; i < RPT; ++i)
+                *reinterpret_cast<float4*>(St + (size_t)(rg + RG * i) * D + 4 * cg) = s[i];
+        }
     }   // tokens
 
     if (MULTI) {   // the state back over the same addresses
