@@ -20,7 +20,8 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 constexpr int D = 128;      // head dim (dk = dv)
 constexpr int C = 64;       // chunk
 constexpr int NT = 256;     // threads per workgroup (both kernels)
-constexpr int SK = D + 8;   // padded row stride (elements) of [64][128] bf16 tiles
+constexpr int SK = D + 16;  // row stride (elements) of the staged k / q rows: 288 bytes, so the
+                            // Gram operand reads (16 rows at a time) hit distinct LDS banks
 constexpr int SC = C + 8;   // padded row stride of [*][64] bf16 tiles
 
 // Workspace record per (b, value head, chunk): T and P (64x64 bf16 in
@@ -137,9 +138,11 @@ struct PrepSmem {
             uint16_t Qr[C][SK];       // raw q rows
         } in;
         struct {
-            float AfT[GH][4][16][16];      // A diagonal blocks (fp32), transposed: [head][block][s][r]
-            uint16_t Ab[GH][6][16][16];    // A blocks below the diagonal (bf16)
-            uint16_t Tl[GH][10][16][16];   // T blocks on and below the diagonal (bf16)
+            // per head, padded by 32 bytes so that the heads' blocks start on
+            // different LDS banks (lanes of different heads read them together)
+            struct { float v[4][16][16]; float pad[8]; } AfT[GH];         // A diagonal blocks (fp32), transposed: [block][s][r]
+            struct { uint16_t v[6][16][16]; uint16_t pad[16]; } Ab[GH];   // A blocks below the diagonal (bf16)
+            struct { uint16_t v[10][16][16]; uint16_t pad[16]; } Tl[GH];  // T blocks on and below the diagonal (bf16)
         } tri;
     };
     float rk[C], rq[C];
@@ -200,9 +203,9 @@ __device__ __forceinline__ void gate_tiles(PrepSmem& sm, const f32x4 (&gram)[5],
                 }
             } else if (a == bb) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) sm.tri.AfT[hh][a][4 * g + t][n] = val[t];
+                for (int t = 0; t < 4; ++t) sm.tri.AfT[hh].v[a][4 * g + t][n] = val[t];
             } else {
-                *reinterpret_cast<s16x4*>(&sm.tri.Ab[hh][ab_idx(a, bb)][n][4 * g]) = pack4(val);
+                *reinterpret_cast<s16x4*>(&sm.tri.Ab[hh].v[ab_idx(a, bb)][n][4 * g]) = pack4(val);
             }
         }
     }
