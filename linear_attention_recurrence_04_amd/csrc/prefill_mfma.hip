@@ -129,12 +129,20 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     const int g = lane >> 4;
     const int n = lane & 15;
 
-    int lid = blockIdx.x;
-    if (xcd_remap) {  // consecutive logical ids on one XCD (dispatch is round-robin over 8)
-        const int per = gridDim.x >> 3;
-        lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    }
     constexpr int NB = D / BVS;          // column blocks per head
+    int lid = blockIdx.x;
+    if (xcd_remap) {
+        // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx & 7).
+        // The G = (Hv / Hk) * NB workgroups of one (sequence, key head) read
+        // the same k and q lines, so they go to one XCD and share its L2;
+        // groups are dealt to the XCDs in turn and each XCD runs its groups in
+        // order, so every XCD starts with the first sequences (a batch sorted
+        // by decreasing length starts its longest chains first everywhere).
+        // Needs the number of groups B * Hk to be a multiple of 8.
+        const int G = (Hv / Hk) * NB;
+        const int kk = blockIdx.x >> 3;
+        lid = ((kk / G) * 8 + (blockIdx.x & 7)) * G + kk % G;
+    }
     const int bh = lid / NB;
     const int j0 = (lid % NB) * BVS;
     const int b = bh / Hv;
@@ -556,7 +564,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
     }
     if (err != hipSuccess) return err;
     const int scan_blocks = a.B * a.Hv * (D / BVS);
-    const int remap = (scan_blocks % 8 == 0) ? 1 : 0;
+    const int remap = ((a.B * a.Hk) % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL(chunk_scan_kernel, dim3(scan_blocks), dim3(SNT), 0, stream,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
                        static_cast<const bf16_t*>(a.v), ws, a.h0, a.hT,
