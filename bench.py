@@ -461,7 +461,7 @@ def main():
         ms_d = bench_decode(torch, gdn, d, args.decode_steps, min(args.warmup, 10) or 1)
         nb = decode_bytes(d)
         gbps_d = nb / (ms_d * 1e-3) / 1e9
-        src_d = source_hash("decode.hip")
+        src_d = source_hash("decode.hip", "gdn_device.h")
         result["decode"] = {
             "workload": d.name, "steps": args.decode_steps,
             "us_per_step": round(ms_d * 1e3, 3),

@@ -108,9 +108,9 @@ def gdn_chunk_prefill_variant(problem: GdnProblem) -> str:
 
 # kernel variant -> (kernel symbol, arithmetic, source files under csrc/)
 VARIANTS = {
-    "generic_f32": ("prefill_generic_kernel", "fp32-valu", ("prefill_generic.hip",)),
+    "generic_f32": ("prefill_generic_kernel", "fp32-valu", ("prefill_generic.hip", "gdn_device.h")),
     "mfma_bf16": ("chunk_prep_kernel+chunk_scan_kernel", "bf16-mfma",
-                  ("prefill_mfma.hip", "prefill_mfma_common.h", "prefill_prep.inc")),
+                  ("prefill_mfma.hip", "prefill_mfma_common.h", "prefill_prep.inc", "gdn_device.h")),
 }
 
 

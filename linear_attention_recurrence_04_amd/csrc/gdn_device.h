@@ -46,6 +46,14 @@ __device__ __forceinline__ float raw_log_decay(float a, float A_log, float dt_bi
 }
 __device__ __forceinline__ float raw_beta(float b) { return 1.0f / (1.0f + expf(-b)); }
 
+// A token's log decay as the chunked kernels use it.  They exponentiate
+// differences of in-chunk prefix sums of log g, and a token with g = 0
+// (log g = -inf) would make such a difference -inf - (-inf) = NaN.  Below -87,
+// g = exp(log g) is already under the smallest normal fp32 (about 1.2e-38), so
+// holding log g at -87 there changes a result only far below fp32 rounding.
+// Written as a comparison so that a NaN passes through unchanged.
+__device__ __forceinline__ float chunk_log_decay(float lg) { return lg < -87.f ? -87.f : lg; }
+
 // Tokens of sequence b on the token axis: [first, first + count).  Without
 // cu_seqlens sequence b is tokens [b T, b T + T).  With them (packed
 // variable-length batch) the bounds are clamped into [0, total] and the count

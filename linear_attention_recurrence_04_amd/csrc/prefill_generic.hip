@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(
                 lgv = raw_log_decay(lgv, A_log[h], dt_bias[h]);
                 btv = raw_beta(btv);
             }
-            lgs[tid] = lgv;   // padding rows: g = 1, beta = 0, k = q = 0
+            lgs[tid] = chunk_log_decay(lgv);   // padding rows: g = 1, beta = 0, k = q = 0
             bts[tid] = btv;
         }
         __syncthreads();

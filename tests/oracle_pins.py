@@ -133,6 +133,31 @@ def pin_no_write_closed_form(lib):
         assert _rel(hT[0, h], G[-1] * h0[0, h]) < 1e-13
 
 
+
+def pin_closed_gate(lib):
+    """g = 0 (log g = -inf) forgets the state before the write.  All gates
+    closed: S_t = beta_t k_hat_t v_t^T, so o_t = beta_t (k_hat_t . q_hat_t) v_t.
+    One closed token at t0: the run from t0 on is a fresh run from a zero
+    state (bitwise)."""
+    rng = _rng(17)
+    B, T, Hk, Hv, d = 1, 12, 1, 2, 5
+    q, k, v, log_g, beta, h0 = _inputs(rng, B, T, Hk, Hv, d, d, "qwen")
+    closed = np.full_like(log_g, -np.inf)
+    o, hT = oracle.gdn_sequential(q, k, v, closed, beta, h0, lib=lib)
+    qh, kh = _unit(q), _unit(k)
+    kq = np.sum(kh[0, :, 0] * qh[0, :, 0], axis=-1)
+    for h in range(Hv):
+        assert _rel(o[0, :, h], (beta[0, :, h] * kq)[:, None] * v[0, :, h]) < 1e-14
+        assert _rel(hT[0, h], beta[0, -1, h] * np.outer(kh[0, -1, 0], v[0, -1, h])) < 1e-14
+    t0 = 5
+    lg = log_g.copy()
+    lg[:, t0, :] = -np.inf
+    o, hT = oracle.gdn_sequential(q, k, v, lg, beta, h0, lib=lib)
+    o2, hT2 = oracle.gdn_sequential(q[:, t0:], k[:, t0:], v[:, t0:], lg[:, t0:], beta[:, t0:], None,
+                                    lib=lib)
+    assert np.array_equal(o[:, t0:], o2) and np.array_equal(hT, hT2)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
+
 def pin_orthonormal_overwrite(lib):
     """k_t = e_t, g = 1, beta = 1: after d steps the state's rows are the v_t."""
     rng = _rng(4)
@@ -353,6 +378,7 @@ PINS = [
     pin_matrix_form,
     pin_unit_key_readback,
     pin_no_write_closed_form,
+    pin_closed_gate,
     pin_orthonormal_overwrite,
     pin_scalar_recurrence,
     pin_exact_example,

@@ -144,6 +144,25 @@ def test_empty_and_degenerate():
     assert_parity(host(o), o_ref, host(hT), h_ref, "f32", "zero rows")
 
 
+
+@pytest.mark.parametrize("dtype,d,C", [("f32", 64, 32), ("bf16", 128, 64)])
+def test_closed_gate_tokens(dtype, d, C):
+    """g = 0 (log g = -inf) at isolated tokens, over a whole chunk, and for one
+    head throughout: the chunked kernels (generic fp32, bf16 MFMA) match the
+    oracle, whose gate is exp(-inf) = 0, with no NaN from the in-chunk decay
+    differences."""
+    say(f"closed gates dtype={dtype} d={d} C={C}")
+    T = 3 * C + 5
+    inp = gi.custom_prefill(1, T, 1, 3, d, d, seed=11, dtype=dtype, gate="qwen", h0="normal")
+    lg = inp["log_g"]
+    lg[0, [0, 7, C - 1, C + 3, 2 * C + 2], 0] = -np.inf
+    lg[0, C:2 * C, 1] = -np.inf
+    lg[0, :, 2] = -np.inf
+    o, hT = run_prefill(inp, dtype, C)
+    o_ref, h_ref = run_oracle(inp)
+    assert np.all(np.isfinite(o_ref)) and np.all(np.isfinite(h_ref))
+    assert_parity(host(o), o_ref, host(hT), h_ref, dtype, "closed gates")
+
 def test_nan_stays_in_its_head():
     inp = gi.custom_prefill(1, 90, 1, 3, 64, 64, seed=8, dtype="f32", gate="qwen", h0="normal")
     inp["log_g"][0, 40, 1] = np.nan
