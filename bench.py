@@ -9,8 +9,12 @@ under "decode" as state-update HBM GB/s and tokens/s.  The same prefill call
 storing a state checkpoint every 512 tokens (gdn_chunk_prefill_ckpt) is timed
 too and reported under "checkpoints", and the call that forms the gates from
 raw projections (gdn_chunk_prefill_gated) under "raw_gates", and decode with
-4 tokens per call (gdn_decode_multi) under "decode_multi", and a packed batch
-of 8 sequences of different lengths (gdn_chunk_prefill_varlen) under "varlen".
+4 tokens per call (gdn_decode_multi) under "decode_multi", a packed batch
+of 8 sequences of different lengths (gdn_chunk_prefill_varlen) under "varlen",
+the 0.8B head shape (T=2048, 16/16 heads) under "prefill_0.8b", and a
+131,072-token prompt processed as 256 consecutive 512-token calls carrying the
+state in place, with the state checkpointed after every call, under
+"long_context".
 
 Inputs are seeded synthetic tensors already resident in HBM when the timed
 region starts.  Kernel time comes from HIP events recorded on the stream the
@@ -195,6 +199,45 @@ def bench_prefill_varlen(torch, gdn, p, steps, warmup):
     log(f"varlen prefill: timing {steps} steps")
     return time_stream(torch, call, steps) / steps
 
+
+
+LONG_DISTINCT_SEGMENTS = 32   # seeded 512-token segments, cycled over the 256 calls
+
+
+def bench_long_context(torch, gdn, p, warmup):
+    """Long prompt processed as consecutive fixed-size calls carrying the fp32
+    state in place (h0 and hT the same tensor), the state copied to a
+    checkpoint bank after every call.  Returns ms for the whole prompt."""
+    Tc = p.extra["call_tokens"]
+    ncalls = p.T // Tc
+    log(f"long context {p.name}: generating {LONG_DISTINCT_SEGMENTS} segments")
+    segs = []
+    for c in range(LONG_DISTINCT_SEGMENTS):
+        s = gi.make_long_segment(p, 0, c)
+        dv = {n: torch.from_numpy(s[n]).cuda() for n in ("q", "k", "v", "log_g", "beta")}
+        for n in ("q", "k", "v"):
+            dv[n] = dv[n].to(torch.bfloat16)
+        segs.append(dv)
+    h = torch.zeros((p.B, p.Hv, p.dk, p.dv), dtype=torch.float32, device="cuda")
+    bank = torch.empty((ncalls, p.B, p.Hv, p.dk, p.dv), dtype=torch.float32, device="cuda")
+    out = torch.empty((p.B, Tc, p.Hv, p.dv), dtype=torch.bfloat16, device="cuda")
+    prob = gdn.make_problem(p.B, Tc, p.Hk, p.Hv, p.dk, p.dv, chunk=p.chunk)
+    ws = torch.empty(max(gdn.gdn_chunk_prefill_workspace_bytes(prob), 1), dtype=torch.uint8,
+                     device="cuda")
+
+    def prompt():
+        h.zero_()
+        for c in range(ncalls):
+            s = segs[c % LONG_DISTINCT_SEGMENTS]
+            gdn.gdn_chunk_prefill(s["q"], s["k"], s["v"], s["log_g"], s["beta"], h, chunk=p.chunk,
+                                  out=out, hT=h, workspace=ws)
+            bank[c].copy_(h)
+
+    for _ in range(max(warmup, 1)):
+        prompt()
+    torch.cuda.synchronize()
+    log(f"long context: timing 3 prompts of {ncalls} calls")
+    return time_stream(torch, prompt, 3) / 3, ncalls
 
 def measured_peaks(torch):
     """Achievable figures on this GPU, for fractions against measured as well as
@@ -456,6 +499,28 @@ def main():
             "vs_one_16384_token_sequence": round(ms / ms_v, 3),
         }
         log(f"varlen prefill: {ms_v:.3f} ms/call, {result['varlen']['tokens_per_s']:.0f} tok/s")
+        # the 0.8B head shape (16 key = 16 value heads, 2048 tokens): 64 scan
+        # workgroups, a short chain of 32 chunks
+        p8 = gi.QWEN08B_PREFILL
+        ms_8, _ = bench_prefill(torch, gdn, p8, args.steps, args.warmup)
+        result["prefill_0.8b"] = {
+            "workload": p8.name, "ms_per_call": round(ms_8, 4),
+            "tokens_per_s": round(p8.B * p8.T / (ms_8 * 1e-3), 1),
+            "hbm_frac": round(prefill_bytes(p8) / (ms_8 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 5),
+            "bf16_mfma_frac": round(prefill_useful_flops(p8) / (ms_8 * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+        }
+        log(f"0.8B prefill: {ms_8 * 1e3:.1f} us/call")
+        # the long prompt: 256 consecutive 512-token calls, state carried and checkpointed
+        pl = gi.QWEN27B_LONG
+        ms_l, ncalls = bench_long_context(torch, gdn, pl, args.warmup)
+        result["long_context"] = {
+            "workload": pl.name, "calls": ncalls, "tokens_per_call": pl.extra["call_tokens"],
+            "distinct_segments": LONG_DISTINCT_SEGMENTS,
+            "ms_per_prompt": round(ms_l, 4), "us_per_call": round(ms_l * 1e3 / ncalls, 3),
+            "tokens_per_s": round(pl.B * pl.T / (ms_l * 1e-3), 1),
+            "state_checkpoint_bank_bytes": ncalls * pl.B * pl.Hv * pl.dk * pl.dv * 4,
+        }
+        log(f"long context: {ms_l:.3f} ms per prompt, {ms_l * 1e3 / ncalls:.1f} us per call")
 
     if args.only in ("all", "decode"):
         ms_d = bench_decode(torch, gdn, d, args.decode_steps, min(args.warmup, 10) or 1)
