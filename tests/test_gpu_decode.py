@@ -53,6 +53,36 @@ def test_decode_steps_match_oracle(dtype, d, Hk, Hv):
         assert per_head_rel(host(state), h_ref, (0, 1)) <= BF16_REL
 
 
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_decode_closed_gates(dtype, d):
+    """g = 0 (log g = -inf) for some (sequence, head) pairs at some steps: the
+    state is forgotten before the write, as in the oracle (exp(-inf) = 0)."""
+    torch = torch_mod()
+    p = gi.DecodeProblem("t", 3, 1, 3, d, d, 6, dtype)
+    say(f"decode closed gates {dtype} d={d}")
+    steps = gi.make_decode_steps(p, 4)
+    steps["log_g"][1][0, 1] = -np.inf
+    steps["log_g"][3][:, 2] = -np.inf
+    steps["log_g"][4][2, :] = -np.inf
+    state0 = gi.make_decode_state(p, 4)
+    state = dev32(state0)
+    outs = []
+    for s in range(p.steps):
+        outs.append(gdn.gdn_decode_step(dev(steps["q"][s], dtype), dev(steps["k"][s], dtype),
+                                        dev(steps["v"][s], dtype), dev32(steps["log_g"][s]),
+                                        dev32(steps["beta"][s]), state))
+    torch.cuda.synchronize()
+    o_gpu = np.stack([host(o) for o in outs])
+    o_ref, h_ref = _oracle_steps(steps, state0, 0, p.steps)
+    assert np.all(np.isfinite(o_ref)) and np.all(np.isfinite(o_gpu))
+    mo, mh = metrics(o_gpu, o_ref), metrics(host(state), h_ref)
+    say(f"  o={mo} state={mh}")
+    if dtype == "f32":
+        assert mo["max_abs"] <= F32_MAX_ABS and mh["max_abs"] <= F32_MAX_ABS
+    else:
+        assert mo["rel_fro"] <= BF16_REL and mh["rel_fro"] <= BF16_REL
+
 def test_decode_equals_prefill_of_one_token(monkeypatch):
     """A one-token prefill and a decode step agree: both within the bar of the
     oracle, and within fp32 rounding of each other on the fp32 prefill kernel."""
