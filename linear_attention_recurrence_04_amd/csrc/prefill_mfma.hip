@@ -57,9 +57,10 @@ namespace mfma_prefill {
 // scan: one workgroup per (b, value head h, 32 state columns), in three roles:
 //  * two state waves (one per 16-column strip): K S, X, Delta = T X and the
 //    state update, the chain that carries the state from chunk to chunk;
-//  * two output waves (one per strip), one chunk behind: Q S and P Delta from
-//    the bf16 state and Delta operands the state waves leave in LDS, and the
-//    output stores;
+//  * two output waves (one per half of the chunk's 64 rows, both strips), one
+//    chunk behind: Q S and P Delta from the bf16 state and Delta operands the
+//    state waves leave in LDS, and the output stores.  Splitting by rows
+//    rather than by strips lets each read only half of the q rows and of P;
 //  * four loader waves: direct global -> LDS loads of the next chunk's inputs
 //    into double-buffered LDS, and cache-line touches of a chunk further
 //    ahead.
@@ -463,71 +464,87 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     }
 
     // ======================= output waves =======================
+    // Output wave `half` forms rows 32 half .. 32 half + 31 of the chunk's
+    // output for both strips, so each reads half of the q rows and of P.
+    // Rows 0..31 of P are zero past column 31, so the first half needs only
+    // the first k step of P Delta.
+    const int half = strip;
     for (int c = 0; c <= NTb; ++c) {
         if (c >= 1) {
             const int cc = c - 1;
             const QSet& B = sm.qs[cc & 1];
-            // ---- operands: state and Delta from the state wave, q rows, P, gates
-            bf16x8 SB[4], aq[4];
+            bf16x8 SB[NSTRIP][4], aq[2];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) SB[ks] = sm.Sx[cc & 1][strip][ks][lane];
+            for (int ii = 0; ii < 2; ++ii)
+                aq[ii] = __builtin_bit_cast(bf16x8, B.Q[(16 * (2 * half + ii) + n) * 16 + (g ^ sn)]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) aq[i] = __builtin_bit_cast(bf16x8, B.Q[(16 * i + n) * 16 + (g ^ sn)]);
-            f32x4 QS[4];
+            for (int st = 0; st < NSTRIP; ++st)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) QS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            // ---- Q S
+                for (int ks = 0; ks < 4; ++ks) SB[st][ks] = sm.Sx[cc & 1][st][ks][lane];
+            f32x4 QS[NSTRIP][2];
+#pragma unroll
+            for (int st = 0; st < NSTRIP; ++st)
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) QS[st][ii] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                bf16x8 nq[4];
+                bf16x8 nq[2];
                 if (ks < 3) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        nq[i] = __builtin_bit_cast(bf16x8, B.Q[(16 * i + n) * 16 + ((4 * (ks + 1) + g) ^ sn)]);
+                    for (int ii = 0; ii < 2; ++ii)
+                        nq[ii] = __builtin_bit_cast(bf16x8, B.Q[(16 * (2 * half + ii) + n) * 16 + ((4 * (ks + 1) + g) ^ sn)]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) QS[i] = mfma32(aq[i], SB[ks], QS[i]);
+                for (int st = 0; st < NSTRIP; ++st)
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) QS[st][ii] = mfma32(aq[ii], SB[st][ks], QS[st][ii]);
                 __builtin_amdgcn_sched_barrier(0);
                 if (ks < 3) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) aq[i] = nq[i];
+                    for (int ii = 0; ii < 2; ++ii) aq[ii] = nq[ii];
                 }
             }
-            bf16x8 ap0[4], ap1[2];
+            bf16x8 ap0[2], ap1[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ap0[i] = __builtin_bit_cast(bf16x8, B.P[imgq(16 * i + n, g)]);
-            ap1[0] = __builtin_bit_cast(bf16x8, B.P[imgq(32 + n, 4 + g)]);
-            ap1[1] = __builtin_bit_cast(bf16x8, B.P[imgq(48 + n, 4 + g)]);
-            const bf16x8 DB0 = sm.Dx[cc & 1][strip][0][lane];
-            const bf16x8 DB1 = sm.Dx[cc & 1][strip][1][lane];
-            f32x4 grq[4];
+            for (int ii = 0; ii < 2; ++ii) {
+                ap0[ii] = __builtin_bit_cast(bf16x8, B.P[imgq(16 * (2 * half + ii) + n, g)]);
+                if (half) ap1[ii] = __builtin_bit_cast(bf16x8, B.P[imgq(32 + 16 * ii + n, 4 + g)]);
+            }
+            f32x4 grq[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) grq[i] = *reinterpret_cast<const f32x4*>(&B.gate[16 * i + 4 * g]);
-            // ---- O = Gamma rq Q S + P Delta
-            f32x4 O4[4];
+            for (int ii = 0; ii < 2; ++ii)
+                grq[ii] = *reinterpret_cast<const f32x4*>(&B.gate[16 * (2 * half + ii) + 4 * g]);
+            uint16_t (*Ot)[OS] = sm.Os;   // each output wave reads back only its own rows
 #pragma unroll
-            for (int i = 0; i < 4; ++i) O4[i] = mfma32(ap0[i], DB0, grq[i] * QS[i]);
-            O4[2] = mfma32(ap1[0], DB1, O4[2]);
-            O4[3] = mfma32(ap1[1], DB1, O4[3]);
-            uint16_t (*Ot)[OS] = sm.Os;   // each output wave reads back only its own columns
+            for (int st = 0; st < NSTRIP; ++st) {
+                const bf16x8 DB0 = sm.Dx[cc & 1][st][0][lane];
+                f32x4 O4[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int ii = 0; ii < 2; ++ii) O4[ii] = mfma32(ap0[ii], DB0, grq[ii] * QS[st][ii]);
+                if (half) {
+                    const bf16x8 DB1 = sm.Dx[cc & 1][st][1][lane];
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    Ot[16 * i + 4 * g + t][SW * strip + n] = static_cast<uint16_t>(bfbits(q_scale * O4[i][t]));
-            // ---- the strip's 64 rows x 32 bytes back from LDS (this wave's own
-            //      writes, so no barrier) and to HBM in 16-byte pieces
+                    for (int ii = 0; ii < 2; ++ii) O4[ii] = mfma32(ap1[ii], DB1, O4[ii]);
+                }
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        Ot[16 * (2 * half + ii) + 4 * g + t][SW * st + n] =
+                            static_cast<uint16_t>(bfbits(q_scale * O4[ii][t]));
+            }
+            // ---- the wave's 32 rows x 64 bytes back from LDS (its own writes,
+            //      so no barrier) and to HBM in 16-byte pieces
             const int t0 = cc * C;
             const int L = min(C, Tb - t0);
-            bf16_t* oc = obase + (size_t)t0 * rowv + SW * strip;
+            bf16_t* oc = obase + (size_t)t0 * rowv;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const int r = (lane >> 1) + 32 * u;
-                const int c8 = 8 * (lane & 1);
+                const int r = 32 * half + (lane >> 2) + 16 * u;
+                const int c8 = 8 * (lane & 3);
                 if (r < L)
-                    *reinterpret_cast<uint4*>(oc + r * rowv + c8) =
-                        *reinterpret_cast<const uint4*>(&Ot[r][SW * strip + c8]);
+                    *reinterpret_cast<uint4*>(oc + r * rowv + c8) = *reinterpret_cast<const uint4*>(&Ot[r][c8]);
             }
         }
         __syncthreads();
