@@ -235,17 +235,23 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
         // Cache-line touches (4-byte loads into a scratch row of LDS) of the
         // chunk TOUCH_AHEAD chunks ahead, so that its direct loads find the
         // lines in L2 instead of waiting on HBM.  Each line is touched by one
-        // workgroup of those that share it: k and q lines by the first column
-        // block of the key head's first value head, the T, P and gate record
-        // by the head's first column block, v lines (128 bytes = two column
-        // blocks) by the even column blocks.  A wave touches two sets of
-        // lines or none.
+        // workgroup of those that share it, and the sets are dealt out so that
+        // no workgroup of a key head's group touches more than one (k and q
+        // both only when a key head has a single value head): the T, P and
+        // gate record by the head's column block 0, the v lines of columns
+        // 0..63 and 64..127 (128 bytes each) by column blocks 1 and 3, the k
+        // lines by column block 2 of the group's first value head, the q
+        // lines by column block 2 of its second.  A wave touches two lines
+        // per lane or none.
         constexpr int TOUCH_AHEAD = 3;
-        const bool first_block = (j0 == 0);
+        const int jb = j0 / BVS;               // column block
+        const int hh = h % (Hv / Hk);          // value head within the key head's group
         bool toucher;
-        if (lw == 0) toucher = first_block;
-        else if (lw == 1) toucher = (j0 % 64) == 0;
-        else toucher = first_block && (h % (Hv / Hk)) == 0;
+        if (lw == 0) toucher = (jb == 0);
+        else if (lw == 1) toucher = (jb == 1 || jb == 3);
+        else if (lw == 2) toucher = (jb == 2 && hh == 0);
+        else toucher = (jb == 2 && hh == min(1, Hv / Hk - 1));
+        const bf16_t* vline = vbase - (j0 & 63);   // the 128-byte v line holding the columns
         auto touch = [&](int chunk) __attribute__((always_inline)) {
             const int t0 = chunk * C;
             const int row = t0 + min(lane, Tb - t0 - 1);
@@ -255,8 +261,8 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 lds_load4(rec + 128 * lane, sink);
                 lds_load4(rec + 128 * min(64 + lane, WS_REC / 128 - 1), sink);
             } else if (lw == 1) {
-                lds_load4(vbase + (size_t)row * rowv, sink);
-                lds_load4(vbase + (size_t)row * rowv + 32, sink);   // same line: keeps two per toucher
+                lds_load4(vline + (size_t)row * rowv, sink);
+                lds_load4(vline + (size_t)row * rowv + 32, sink);   // same line: keeps two per toucher
             } else {
                 const bf16_t* base = (lw == 2) ? kbase : qbase;
                 lds_load4(base + (size_t)row * rowk, sink);
