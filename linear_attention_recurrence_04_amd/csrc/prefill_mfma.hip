@@ -191,10 +191,11 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
         kq_offsets(offq, C - 1);
         v_offsets(C - 1);
 
-        // The k side of a chunk is 7 direct loads per loader wave (k 4, T 2
-        // or 1, v 1, gates 1 on one wave; the fourth wave repeats its last k
-        // block), so that one wait count fits every wave.
+        // The k side of a chunk is 27 direct loads of 1 KiB: k 16, T 6, v 4,
+        // gates 1; seven on loader waves 0..2 (the gates on wave 2) and six
+        // on wave 3, which also issues the workgroup's cache-line touches.
         constexpr int NKLOADS = 7;
+        constexpr int NKLOADS3 = 6;
         auto load_k = [&](int chunk, int slot) __attribute__((always_inline)) {
             if (chunk == NTb - 1) {   // the last chunk: clamp its rows
                 kq_offsets(offk, last_rows);
@@ -215,7 +216,6 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
 #pragma unroll
             for (int u = 0; u < NVB; ++u) lds_load16(vc + offv[u], &B.V[64 * (lw + LWAVES * u)]);
             if (lw == 2) lds_load16(rec + WS_G + 16 * lane, B.gate);   // 1 KiB
-            if (lw == 3) lds_load16(kc + offk[NKB - 1], &B.K[64 * (lw + LWAVES * (NKB - 1))]);   // count filler
         };
         auto load_q = [&](int chunk, int slot) __attribute__((always_inline)) {
             if (chunk == NTb - 1) kq_offsets(offq, last_rows);
@@ -241,35 +241,40 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
         // gate record by the head's column block 0, the v lines of columns
         // 0..63 and 64..127 (128 bytes each) by column blocks 1 and 3, the k
         // lines by column block 2 of the group's first value head, the q
-        // lines by column block 2 of its second.  A wave touches two lines
-        // per lane or none.
+        // lines by column block 2 of its second.  Loader wave 3 issues them,
+        // two lines per lane per set.
         constexpr int TOUCH_AHEAD = 3;
         const int jb = j0 / BVS;               // column block
         const int hh = h % (Hv / Hk);          // value head within the key head's group
-        bool toucher;
-        if (lw == 0) toucher = (jb == 0);
-        else if (lw == 1) toucher = (jb == 1 || jb == 3);
-        else if (lw == 2) toucher = (jb == 2 && hh == 0);
-        else toucher = (jb == 2 && hh == min(1, Hv / Hk - 1));
+        const bool t_rec = (jb == 0);
+        const bool t_v = (jb == 1 || jb == 3);
+        const bool t_k = (jb == 2 && hh == 0);
+        const bool t_q = (jb == 2 && hh == min(1, Hv / Hk - 1));
+        const bool toucher = (lw == 3) && (t_rec || t_v || t_k || t_q);
+        const bool two_sets = t_k && t_q;      // a key head with a single value head
         const bf16_t* vline = vbase - (j0 & 63);   // the 128-byte v line holding the columns
         auto touch = [&](int chunk) __attribute__((always_inline)) {
             const int t0 = chunk * C;
             const int row = t0 + min(lane, Tb - t0 - 1);
             uint32_t* sink = sm.sink[lw];
             const unsigned char* rec = rec0 + (size_t)chunk * WS_REC;   // 106 lines of 128 bytes
-            if (lw == 0) {
+            if (t_rec) {
                 lds_load4(rec + 128 * lane, sink);
                 lds_load4(rec + 128 * min(64 + lane, WS_REC / 128 - 1), sink);
-            } else if (lw == 1) {
+            } else if (t_v) {
                 lds_load4(vline + (size_t)row * rowv, sink);
-                lds_load4(vline + (size_t)row * rowv + 32, sink);   // same line: keeps two per toucher
+                lds_load4(vline + (size_t)row * rowv + 32, sink);   // same line: keeps two per set
             } else {
-                const bf16_t* base = (lw == 2) ? kbase : qbase;
-                lds_load4(base + (size_t)row * rowk, sink);
-                lds_load4(base + (size_t)row * rowk + 64, sink);
+                if (t_k) {
+                    lds_load4(kbase + (size_t)row * rowk, sink);
+                    lds_load4(kbase + (size_t)row * rowk + 64, sink);
+                }
+                if (t_q) {
+                    lds_load4(qbase + (size_t)row * rowk, sink);
+                    lds_load4(qbase + (size_t)row * rowk + 64, sink);
+                }
             }
         };
-        constexpr int NTOUCH = 2;
         // iteration c: the state waves work on chunk c and the output waves on
         // chunk c - 1; load the q side of chunk c, then the k side of chunk
         // c + 2, then the touches.  Operations complete in issue order, so
@@ -292,10 +297,20 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
             __builtin_amdgcn_sched_barrier(0);
             const bool tload = toucher && c + TOUCH_AHEAD < NTb;
             if (tload) touch(c + TOUCH_AHEAD);
-            if (kload && tload) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NKLOADS + NTOUCH));
-            else if (kload) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NKLOADS));
-            else if (tload) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NTOUCH));
-            else __builtin_amdgcn_s_waitcnt(0);
+            if (lw != 3) {
+                if (kload) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NKLOADS));
+                else __builtin_amdgcn_s_waitcnt(0);
+            } else if (kload && tload) {
+                if (two_sets) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NKLOADS3 + 4));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(NKLOADS3 + 2));
+            } else if (kload) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(NKLOADS3));
+            } else if (tload) {
+                if (two_sets) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
+            } else {
+                __builtin_amdgcn_s_waitcnt(0);
+            }
             // a plain barrier: a fenced one would also wait for the loads
             // and touches still in flight
             asm volatile("" ::: "memory");
