@@ -16,24 +16,30 @@
 // once and written once per call, and optionally also stored after every
 // token (the per-token states a verifier rolls back to).
 //
-// Mapping: one workgroup of 256 threads per (b, h).  A thread owns a float4
+// Mapping: one workgroup of NT threads per (b, h).  A thread owns a float4
 // column strip of D/RG rows (RG = row groups), held in VGPRs between the read
 // and the write; rows are interleaved so each wave load covers whole 512-byte
 // rows (fully coalesced 16-byte accesses).  Column reductions over the rows
 // combine per-thread partials in LDS in a fixed order (deterministic).
+// NT is 256 for several tokens per call and for head dim 64; a single step
+// at head dim 128 uses 512 threads (8 rows per thread), or 1024 (4 rows) once
+// the whole state no longer fits the 256 MB Infinity Cache and streams from
+// HBM (measured on the 27B head shape: 64 sequences, 201 MB of state, 512
+// threads -2% against 256, 1024 threads +27%; 128 sequences, 403 MB, 1024
+// threads -7%).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 
-template <int D, typename TIn, bool MULTI>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+template <int D, typename TIn, bool MULTI, int NTHR>
+__global__ __launch_bounds__(NTHR) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ log_g, const float* __restrict__ beta,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     float* __restrict__ state, TIn* __restrict__ o, float* __restrict__ states,
     int T, int Hk, int Hv, int l2norm, float q_scale) {
-    constexpr int NT = 256;
+    constexpr int NT = NTHR;
     constexpr int CG = D / 4;     // float4 column groups per row
     constexpr int RG = NT / CG;   // row groups
     constexpr int RPT = D / RG;   // rows per thread
@@ -173,18 +179,31 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
 }
 
+template <int D, typename TIn, int NTHR>
+static void launch_single(const DecodeArgs& a, int blocks, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_step_kernel<D, TIn, false, NTHR>), dim3(blocks), dim3(NTHR), 0, stream,
+                       static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                       static_cast<const TIn*>(a.v), a.log_g, a.beta, a.A_log, a.dt_bias,
+                       a.state, static_cast<TIn*>(a.o), nullptr, 1, a.Hk, a.Hv, a.l2norm, a.q_scale);
+}
+
+// bytes of decode state beyond which a single step streams it from HBM
+constexpr size_t kInfinityCacheBytes = size_t(256) << 20;
+
 template <int D, typename TIn>
 static hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const int blocks = a.B * a.Hv;
     if (blocks == 0 || a.T == 0) return hipSuccess;
-    if (a.T == 1 && !a.states)
-        hipLaunchKernelGGL((decode_step_kernel<D, TIn, false>), dim3(blocks), dim3(256), 0, stream,
-                           static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                           static_cast<const TIn*>(a.v), a.log_g, a.beta, a.A_log, a.dt_bias,
-                           a.state, static_cast<TIn*>(a.o), nullptr, 1, a.Hk, a.Hv, a.l2norm,
-                           a.q_scale);
-    else
-        hipLaunchKernelGGL((decode_step_kernel<D, TIn, true>), dim3(blocks), dim3(256), 0, stream,
+    if (a.T == 1 && !a.states) {
+        if constexpr (D == 128) {
+            const size_t state_bytes = (size_t)blocks * D * D * sizeof(float);
+            if (state_bytes > kInfinityCacheBytes) launch_single<D, TIn, 1024>(a, blocks, stream);
+            else launch_single<D, TIn, 512>(a, blocks, stream);
+        } else {
+            launch_single<D, TIn, 256>(a, blocks, stream);
+        }
+    } else
+        hipLaunchKernelGGL((decode_step_kernel<D, TIn, true, 256>), dim3(blocks), dim3(256), 0, stream,
                            static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                            static_cast<const TIn*>(a.v), a.log_g, a.beta, a.A_log, a.dt_bias,
                            a.state, static_cast<TIn*>(a.o), a.states, a.T, a.Hk, a.Hv, a.l2norm,

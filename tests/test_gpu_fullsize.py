@@ -112,6 +112,35 @@ def test_qwen27b_decode_full_state_then_long_run():
     assert worst <= BF16_REL and rel_state <= BF16_REL
 
 
+
+def test_qwen27b_decode_b128_state_past_the_cache():
+    """B=128, 16/48 heads, d=128: 403 MB of state, more than the 256 MB Infinity
+    Cache, so a single step runs the 1024-thread form of the decode kernel;
+    two steps checked on every head."""
+    torch = torch_mod()
+    p = gi.DecodeProblem("qwen27b_decode_B128_Hk16_Hv48_d128", 128, 16, 48, 128, 128, 2)
+    say("decode B=128 (state past the Infinity Cache)")
+    state0 = gi.make_decode_state(p, 3)
+    state = dev32(state0)
+    steps = gi.make_decode_steps(p, 3)
+    outs = []
+    for s in range(p.steps):
+        outs.append(host(gdn.gdn_decode_step(*(dev(steps[n][s], "bf16") for n in ("q", "k", "v")),
+                                             dev32(steps["log_g"][s]), dev32(steps["beta"][s]), state)))
+    torch.cuda.synchronize()
+    h = state0
+    for s in range(p.steps):
+        o_r, h = oracle.gdn_sequential(*(steps[n][s][:, None] for n in ("q", "k", "v", "log_g", "beta")),
+                                       h, nthreads=NTHREADS)
+        m = metrics(outs[s], o_r[:, 0])
+        say(f"  step {s}: o {m}")
+        assert m["rel_fro"] <= BF16_REL
+        assert per_head_rel(outs[s], o_r[:, 0], (0, 1)) <= BF16_REL
+    h_gpu = host(state)
+    mh = metrics(h_gpu, h)
+    say(f"  state: {mh}")
+    assert mh["rel_fro"] <= BF16_REL and per_head_rel(h_gpu, h, (0, 1)) <= BF16_REL
+
 def test_qwen27b_long_context_512_token_calls():
     """131072 tokens as 256 calls of 512 carrying the fp32 state: outputs and
     final state bitwise equal to one call; every checkpoint of key-head group 5

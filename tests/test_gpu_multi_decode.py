@@ -69,7 +69,11 @@ def test_multi_decode_matches_oracle(dtype, d, Hk, Hv, T):
     for t in range(T):
         check(host(sts[:, t]), st_ref[:, t], dtype, f"state after token {t}")
     assert torch.equal(sts[:, -1], state)
-    # the same tokens as T single decode steps agree to rounding
+    # the same tokens as T single decode steps agree to rounding: the two
+    # kernels sum the column reductions in different orders (256 threads of 16
+    # rows here, 512 or 1024 threads for a single step at head dim 128), so
+    # the fp32 states agree to a few fp32 ulps and a bf16 output may round the
+    # other way (one bf16 ulp, 2^-7 relative)
     state_s = dev32(state0)
     outs = []
     for t in range(T):
@@ -77,7 +81,8 @@ def test_multi_decode_matches_oracle(dtype, d, Hk, Hv, T):
                                         dev(seq["v"][:, t], dtype), dev32(seq["log_g"][:, t]),
                                         dev32(seq["beta"][:, t]), state_s))
     torch.cuda.synchronize()
-    assert np.allclose(host(torch.stack(outs, dim=1)), host(o), rtol=1e-5, atol=1e-6)
+    o_rtol = 2.0 ** -7 if dtype == "bf16" else 1e-5
+    assert np.allclose(host(torch.stack(outs, dim=1)), host(o), rtol=o_rtol, atol=1e-6)
     assert np.allclose(host(state_s), host(state), rtol=1e-5, atol=1e-7)
 
 
