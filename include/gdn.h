@@ -89,7 +89,20 @@ typedef struct {
  * initialisation and are meaningless after the call.  The bf16 MFMA path
  * ("mfma_bf16" below) needs 13568 bytes per (sequence, value head, chunk of
  * 64 tokens): the chunk's triangular inverse, masked Q K^T and gate vectors,
- * computed for all chunks in parallel before the serial pass.
+ * computed for all chunks in parallel before the serial pass; plus one fp32
+ * state per (sequence, value head), handed between the two pieces of a long
+ * call (next paragraph).
+ *
+ * On that path a call of at least 256 chunks on few sequences (no cu_seqlens,
+ * no checkpoints, at most 256 scan workgroups of 32 state columns) runs as two
+ * pieces of whole chunks: the state-independent part of the second piece runs
+ * on a second stream, which the library creates per device on first use and
+ * keeps, while the serial pass works through the first piece.  The caller's
+ * stream waits for it before the call's last kernel, so for the caller the
+ * call is ordered on its stream as one launch is, and the results are
+ * bitwise those of one launch.  A stream under graph capture always gets one
+ * piece, on the caller's stream only.  GDN_PREFILL_PIECES=n in the
+ * environment sets the piece count (1 to 4) for comparisons.
  */
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* problem);
 

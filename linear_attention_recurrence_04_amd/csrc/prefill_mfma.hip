@@ -42,6 +42,9 @@
 //    global -> LDS loads.
 #include "prefill_mfma_common.h"
 
+#include <cstdlib>
+#include <mutex>
+
 namespace gdn {
 namespace mfma_prefill {
 
@@ -122,7 +125,8 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const unsigned char* __restrict__ ws, const float* h0, float* hT, bf16_t* __restrict__ o,
     int T, int NTc, int Hk, int Hv, float q_scale, int xcd_remap,
-    float* __restrict__ ckpt, int ckpt_every, int nck, const int* __restrict__ cu, long long total) {
+    float* __restrict__ ckpt, int ckpt_every, int nck, const int* __restrict__ cu, long long total,
+    int c_first, int n_chunks) {
     __shared__ ScanSmem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -152,9 +156,15 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     size_t tb0;   // first token of sequence b
     int Tb;       // its length (T for equal-length batches)
     seq_span(cu, b, T, total, tb0, Tb);
-    const int NTb = (Tb + C - 1) / C;    // its chunks (records are laid out for NTc)
+    // The launch runs chunks [c_first, c_first + n_chunks) of each sequence,
+    // from the state h0 holds before chunk c_first (checkpoints need the
+    // whole sequence: c_first = 0 with them).
+    const int skip = min(c_first * C, Tb);
+    tb0 += skip;
+    Tb = min(Tb - skip, n_chunks * C);
+    const int NTb = (Tb + C - 1) / C;    // chunks to run (records are laid out for NTc)
     const size_t state_base = (size_t)bh * D * D;
-    const unsigned char* rec0 = ws + (size_t)bh * NTc * WS_REC;
+    const unsigned char* rec0 = ws + ((size_t)bh * NTc + c_first) * WS_REC;
     const bf16_t* kbase = k + (tb0 * Hk + hk) * D;
     const bf16_t* qbase = q + (tb0 * Hk + hk) * D;
     const bf16_t* vbase = v + (tb0 * Hv + h) * D + j0;
@@ -578,37 +588,165 @@ bool prefill_mfma_supported(const PrefillArgs& a) {
     return a.bf16 && a.D == 128 && a.C == 64;
 }
 
-size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv) {
-    const size_t NTc = (size_t)(T + mfma_prefill::C - 1) / mfma_prefill::C;
-    (void)Hk;
-    return (size_t)B * Hv * NTc * mfma_prefill::WS_REC;
+namespace {
+
+using namespace mfma_prefill;
+
+// Records of every (b, value head, chunk), then the fp32 state handed from
+// one piece of a call to the next (below).
+size_t records_bytes(int B, int T, int Hv) {
+    const size_t NTc = (size_t)(T + C - 1) / C;
+    return (size_t)B * Hv * NTc * WS_REC;
 }
 
-hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
-    using namespace mfma_prefill;
-    const int NTc = (a.T + C - 1) / C;
-    const int prep_blocks = a.B * a.Hk * NTc;
-    if (prep_blocks == 0) return hipSuccess;
-    unsigned char* ws = static_cast<unsigned char*>(a.ws);
-    hipError_t err;
-    if (a.A_log) {
-        err = launch_prep_raw(a, NTc, ws, stream);
-    } else {
-        hipLaunchKernelGGL(chunk_prep_kernel, dim3(prep_blocks), dim3(NT), 0, stream,
-                           static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k), a.log_g,
-                           a.beta, nullptr, nullptr, ws, a.T, NTc, a.Hk, a.Hv, a.l2norm, a.cu,
-                           a.total);
-        err = hipGetLastError();
+// A long call on few sequences runs as up to kMaxPieces pieces of whole
+// chunks.  The prep of piece 0 runs first, on the caller's stream; the preps
+// of the later pieces run in order on a second stream owned by the library,
+// and the scan of piece p, on the caller's stream, waits only for the prep of
+// piece p and starts from the fp32 state the scan of piece p - 1 left in the
+// workspace.  The preps of later pieces so run beside the scan of earlier
+// ones, on the compute units the scan leaves free.  The pieces compute
+// exactly what one launch computes: each chunk's records and its step of the
+// chain are the same, and the state passes between pieces unrounded.
+//
+// A scan workgroup holds nearly all of a compute unit's LDS, so a prep
+// workgroup runs only on a unit the scan leaves free.  Measured on MI355X
+// (bf16, head dim 128, one sequence, per call): two pieces take 16 key / 48
+// value heads from 395 to 380 us at T = 16384 and from 776 to 726 us at
+// T = 32768; at T = 8192 they break even and at T = 4096 or 2048 they lose
+// 5 to 11 us (the hand-over between the streams).  Three or four pieces are
+// slower than two at every size tried: at each piece boundary where a later
+// prep is still queued, that prep takes the units the finishing scan frees
+// and the next scan piece waits for them.  Hence two pieces from
+// kPiecesFromChunks chunks on.
+constexpr int kMaxPieces = 4;
+constexpr int kMinPieceChunks = 16;
+constexpr int kPiecesFromChunks = 256;
+
+// The second stream and the events ordering it against the caller's stream:
+// one set per device, created on first use and kept until the process ends.
+// Default priority and no blocking against the legacy null stream.  Calls on
+// different streams of a device share it, so the second piece of one call may
+// wait behind that of a call enqueued before it (never on a later one: every
+// wait is on work enqueued earlier, so no cycle can form).
+struct SideStream {
+    bool tried = false;
+    bool ok = false;
+    hipStream_t stream = nullptr;
+    hipEvent_t start = nullptr;              // prep of piece 0 done
+    hipEvent_t done[kMaxPieces] = {};        // prep of piece p done
+};
+constexpr int kMaxDevices = 64;
+std::mutex side_mutex;                       // held while a call enqueues its pieces
+SideStream side_streams[kMaxDevices];
+
+// The current device's side stream, or nullptr when it cannot be had (called
+// with side_mutex held).
+SideStream* side_stream(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    SideStream& ss = side_streams[dev];
+    if (!ss.tried) {
+        ss.tried = true;
+        // Both streams are on one device and nothing is read by the host, so
+        // the events need device-scope fences only; the default system-scope
+        // fence measured 10 us of idle time per hand-over.
+        const unsigned flags = hipEventDisableTiming | hipEventDisableSystemFence;
+        bool ok = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&ss.start, flags) == hipSuccess;
+        for (int p = 0; p < kMaxPieces; ++p)
+            ok = ok && hipEventCreateWithFlags(&ss.done[p], flags) == hipSuccess;
+        if (!ok) (void)hipGetLastError();   // the call goes on as one piece
+        ss.ok = ok;
     }
-    if (err != hipSuccess) return err;
+    return ss.ok ? &ss : nullptr;
+}
+
+// Pieces for this call: 2 from kPiecesFromChunks chunks on, else 1; always 1
+// for packed batches, checkpoints, calls whose scan already has more than one
+// workgroup per compute unit (no room beside it) and streams under graph
+// capture.  GDN_PREFILL_PIECES=n in the environment sets the count (1 to
+// kMaxPieces, each piece at least kMinPieceChunks chunks) for comparisons.
+int piece_count(const PrefillArgs& a, int NTc, int scan_blocks, hipStream_t stream) {
+    if (a.cu || a.ckpt || scan_blocks > 256) return 1;
+    int want = NTc >= kPiecesFromChunks ? 2 : 1;
+    if (const char* e = getenv("GDN_PREFILL_PIECES")) want = atoi(e);
+    want = want < 1 ? 1 : (want > kMaxPieces ? kMaxPieces : want);
+    while (want > 1 && NTc / want < kMinPieceChunks) --want;
+    if (want == 1) return 1;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+        (void)hipGetLastError();
+        return 1;
+    }
+    return cap == hipStreamCaptureStatusNone ? want : 1;
+}
+
+hipError_t launch_prep(const PrefillArgs& a, int NTc, unsigned char* ws, int c_first,
+                       int n_chunks, hipStream_t stream) {
+    if (a.A_log) return launch_prep_raw(a, NTc, ws, c_first, n_chunks, stream);
+    hipLaunchKernelGGL(chunk_prep_kernel, dim3(a.B * a.Hk * n_chunks), dim3(NT), 0, stream,
+                       static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k), a.log_g,
+                       a.beta, nullptr, nullptr, ws, a.T, NTc, a.Hk, a.Hv, a.l2norm, a.cu,
+                       a.total, c_first, n_chunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const PrefillArgs& a, int NTc, const unsigned char* ws, const float* h0,
+                       float* hT, int c_first, int n_chunks, hipStream_t stream) {
     const int scan_blocks = a.B * a.Hv * (D / BVS);
     const int remap = ((a.B * a.Hk) % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL(chunk_scan_kernel, dim3(scan_blocks), dim3(SNT), 0, stream,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
-                       static_cast<const bf16_t*>(a.v), ws, a.h0, a.hT,
+                       static_cast<const bf16_t*>(a.v), ws, h0, hT,
                        static_cast<bf16_t*>(a.o), a.T, NTc, a.Hk, a.Hv, a.q_scale, remap,
-                       a.ckpt, a.ckpt_every, a.nck, a.cu, a.total);
+                       a.ckpt, a.ckpt_every, a.nck, a.cu, a.total, c_first, n_chunks);
     return hipGetLastError();
+}
+
+}  // namespace
+
+size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv) {
+    (void)Hk;
+    return records_bytes(B, T, Hv) + (size_t)B * Hv * D * D * sizeof(float);
+}
+
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
+    const int NTc = (a.T + C - 1) / C;
+    if (a.B * a.Hk * NTc == 0) return hipSuccess;
+    unsigned char* ws = static_cast<unsigned char*>(a.ws);
+    const int scan_blocks = a.B * a.Hv * (D / BVS);
+    const int P = piece_count(a, NTc, scan_blocks, stream);
+    std::unique_lock<std::mutex> lock(side_mutex, std::defer_lock);
+    SideStream* side = nullptr;
+    if (P > 1) {
+        lock.lock();
+        int dev = -1;
+        if (hipGetDevice(&dev) == hipSuccess) side = side_stream(dev);
+    }
+    if (!side) {
+        const hipError_t err = launch_prep(a, NTc, ws, 0, NTc, stream);
+        if (err != hipSuccess) return err;
+        return launch_scan(a, NTc, ws, a.h0, a.hT, 0, NTc, stream);
+    }
+    // pieces of whole chunks, the first ones one chunk longer
+    int first[kMaxPieces + 1];
+    first[0] = 0;
+    for (int p = 0; p < P; ++p) first[p + 1] = first[p] + NTc / P + (p < NTc % P ? 1 : 0);
+    float* carry = reinterpret_cast<float*>(ws + records_bytes(a.B, a.T, a.Hv));
+    hipError_t err = launch_prep(a, NTc, ws, 0, first[1], stream);
+    if (err == hipSuccess) err = hipEventRecord(side->start, stream);
+    if (err == hipSuccess) err = hipStreamWaitEvent(side->stream, side->start, 0);
+    for (int p = 1; p < P && err == hipSuccess; ++p) {
+        err = launch_prep(a, NTc, ws, first[p], first[p + 1] - first[p], side->stream);
+        if (err == hipSuccess) err = hipEventRecord(side->done[p], side->stream);
+    }
+    for (int p = 0; p < P && err == hipSuccess; ++p) {
+        if (p > 0) err = hipStreamWaitEvent(stream, side->done[p], 0);
+        if (err == hipSuccess)
+            err = launch_scan(a, NTc, ws, p == 0 ? a.h0 : carry, p == P - 1 ? a.hT : carry,
+                              first[p], first[p + 1] - first[p], stream);
+    }
+    return err;
 }
 
 }  // namespace gdn

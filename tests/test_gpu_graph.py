@@ -1,8 +1,9 @@
 """Library calls captured into a HIP graph (torch.cuda.graph) and replayed:
 every replay, with eager work and synchronisation between replays, must give
-bitwise the eager result.  The library enqueues only kernels on the caller's
-stream (no allocation, no memset, no synchronisation), which is what makes
-its calls capturable."""
+bitwise the eager result.  Under capture the library enqueues only kernels
+on the caller's stream (no allocation, no memset, no synchronisation, and a
+long prefill that runs eagerly as two pieces on two streams runs as one
+piece), which is what makes its calls capturable."""
 import numpy as np
 import pytest
 
@@ -51,13 +52,15 @@ def test_decode_steps_in_a_graph():
         assert torch.equal(out, o_ref) and torch.equal(state, s_ref), f"replay {rep}"
 
 
-@pytest.mark.parametrize("dtype,d,C", [("bf16", 128, 64), ("f32", 64, 32)])
-def test_prefill_in_a_graph(dtype, d, C):
+# T = 16400 is 257 chunks of 64: two pieces eagerly, one under capture
+@pytest.mark.parametrize("dtype,d,C,T", [("bf16", 128, 64, 200), ("f32", 64, 32, 200),
+                                         ("bf16", 128, 64, 16400)])
+def test_prefill_in_a_graph(dtype, d, C, T):
     torch = torch_mod()
-    inp = gi.custom_prefill(1, 200, 1, 3, d, d, seed=9, dtype=dtype, gate="qwen", h0="normal")
+    inp = gi.custom_prefill(1, T, 1, 3, d, d, seed=9, dtype=dtype, gate="qwen", h0="normal")
     q, k, v = dev(inp["q"], dtype), dev(inp["k"], dtype), dev(inp["v"], dtype)
     lg, bt, h0 = dev32(inp["log_g"]), dev32(inp["beta"]), dev32(inp["h0"])
-    prob = gdn.make_problem(1, 200, 1, 3, d, d, chunk=C,
+    prob = gdn.make_problem(1, T, 1, 3, d, d, chunk=C,
                             dtype=gdn.GDN_DTYPE_BF16 if dtype == "bf16" else gdn.GDN_DTYPE_F32)
     ws = torch.empty(max(gdn.gdn_chunk_prefill_workspace_bytes(prob), 1), dtype=torch.uint8,
                      device="cuda")

@@ -242,3 +242,58 @@ def test_mfma_gqa_ratios(Hk, Hv):
     o, hT = run_prefill(inp, "bf16", 64)
     o_ref, h_ref = run_oracle(inp)
     assert_parity(host(o), o_ref, host(hT), h_ref, "bf16", f"mfma {Hk}x{Hv}")
+
+
+# 16400 tokens = 257 chunks of 64 (last one ragged): a call this long runs as
+# two pieces (129 + 128 chunks) with the second piece's prep on a second stream
+PIECE_T = 16400
+
+
+@pytest.mark.parametrize("case", ["plain", "zero_state", "in_place", "no_final_state",
+                                  "raw_gates", "three_pieces", "four_pieces"])
+def test_pieces_bitwise_one_launch(monkeypatch, case):
+    """A long call run in pieces gives bitwise the o and hT of one launch
+    (GDN_PREFILL_PIECES=1), whatever the state arguments or the gate form."""
+    torch = torch_mod()
+    B, Hk, Hv, d = 1, 1, 2, 128
+    say(f"pieces {case} T={PIECE_T}")
+    inp = gi.custom_prefill(B, PIECE_T, Hk, Hv, d, d, seed=77, dtype="bf16", gate="qwen",
+                            h0="normal")
+    q, k, v = dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16")
+    lg, bt = dev32(inp["log_g"]), dev32(inp["beta"])
+    raw = gi.make_raw_gates((B, PIECE_T), Hv, seed=78) if case == "raw_gates" else None
+    pieces = {"three_pieces": "3", "four_pieces": "4"}.get(case, "2")
+
+    def call():
+        h0 = None if case == "zero_state" else dev32(inp["h0"])
+        if raw is not None:
+            o, hT, _ = gdn.gdn_chunk_prefill_gated(q, k, v, dev32(raw["a"]), dev32(raw["b"]),
+                                                   dev32(raw["A_log"]), dev32(raw["dt_bias"]), h0)
+        elif case == "in_place":
+            o, hT = gdn.gdn_chunk_prefill(q, k, v, lg, bt, h0, hT=h0)
+            assert hT is h0
+        else:
+            o, hT = gdn.gdn_chunk_prefill(q, k, v, lg, bt, h0,
+                                          want_state=case != "no_final_state")
+        torch.cuda.synchronize()
+        return o, hT
+
+    monkeypatch.setenv("GDN_PREFILL_PIECES", "1")
+    o1, h1 = call()
+    monkeypatch.setenv("GDN_PREFILL_PIECES", pieces)
+    o2, h2 = call()
+    monkeypatch.delenv("GDN_PREFILL_PIECES")
+    assert torch.equal(o1, o2), case
+    if case == "no_final_state":
+        assert h1 is None and h2 is None
+    else:
+        assert torch.equal(h1, h2), case
+
+
+def test_two_pieces_match_oracle():
+    """The default two-piece path on a long ragged call, against the oracle."""
+    inp = gi.custom_prefill(1, PIECE_T, 1, 2, 128, 128, seed=79, dtype="bf16", gate="qwen",
+                            h0="normal")
+    o, hT = run_prefill(inp, "bf16", 64)
+    o_ref, h_ref = run_oracle(inp)
+    assert_parity(host(o), o_ref, host(hT), h_ref, "bf16", f"two pieces T={PIECE_T}")
