@@ -297,3 +297,52 @@ def test_two_pieces_match_oracle():
     o, hT = run_prefill(inp, "bf16", 64)
     o_ref, h_ref = run_oracle(inp)
     assert_parity(host(o), o_ref, host(hT), h_ref, "bf16", f"two pieces T={PIECE_T}")
+
+
+def test_pieces_from_two_threads_on_two_streams():
+    """Two host threads, each on a stream and workspace of its own, enqueue long
+    two-piece calls at the same time, so both share the library's second
+    stream; every result is bitwise that of the same call made alone."""
+    import threading
+    torch = torch_mod()
+    B, Hk, Hv, d, reps = 1, 1, 2, 128, 4
+    say(f"two threads x {reps} calls of T={PIECE_T}")
+    args = []
+    for i in range(2):
+        inp = gi.custom_prefill(B, PIECE_T, Hk, Hv, d, d, seed=90 + i, dtype="bf16", gate="qwen",
+                                h0="normal")
+        a = {n: dev(inp[n], "bf16") for n in ("q", "k", "v")}
+        a.update({n: dev32(inp[n]) for n in ("log_g", "beta", "h0")})
+        args.append(a)
+    ref = [gdn.gdn_chunk_prefill(a["q"], a["k"], a["v"], a["log_g"], a["beta"], a["h0"])
+           for a in args]
+    prob = gdn.make_problem(B, PIECE_T, Hk, Hv, d, d, chunk=64, dtype=gdn.GDN_DTYPE_BF16)
+    ws = [torch.empty(gdn.gdn_chunk_prefill_workspace_bytes(prob), dtype=torch.uint8,
+                      device="cuda") for _ in range(2)]
+    outs = [[torch.empty_like(ref[i][0]) for _ in range(reps)] for i in range(2)]
+    hts = [[torch.empty_like(ref[i][1]) for _ in range(reps)] for i in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        try:
+            a = args[i]
+            for r in range(reps):
+                gdn.gdn_chunk_prefill(a["q"], a["k"], a["v"], a["log_g"], a["beta"], a["h0"],
+                                      out=outs[i][r], hT=hts[i][r], workspace=ws[i],
+                                      stream=streams[i])
+            streams[i].synchronize()
+        except Exception as e:   # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        for r in range(reps):
+            assert torch.equal(outs[i][r], ref[i][0]) and torch.equal(hts[i][r], ref[i][1]), (i, r)
