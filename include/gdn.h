@@ -95,9 +95,10 @@ typedef struct {
  *
  * On that path a call of at least 256 chunks on few sequences (no cu_seqlens,
  * no checkpoints, at most 256 scan workgroups of 32 state columns) runs as two
- * pieces of whole chunks: the state-independent part of the second piece runs
- * on a second stream, which the library creates per device on first use and
- * keeps, while the serial pass works through the first piece.  The caller's
+ * pieces of whole chunks (the second 1.15 times as long as the first): the
+ * state-independent part of the second piece runs on a second stream, which
+ * the library creates per device on first use and keeps, while the serial
+ * pass works through the first piece.  The caller's
  * stream waits for it before the call's last kernel, so for the caller the
  * call is ordered on its stream as one launch is, and the results are
  * bitwise those of one launch.  A stream under graph capture always gets one

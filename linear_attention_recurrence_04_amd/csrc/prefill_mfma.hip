@@ -622,6 +622,16 @@ size_t records_bytes(int B, int T, int Hv) {
 constexpr int kMaxPieces = 4;
 constexpr int kMinPieceChunks = 16;
 constexpr int kPiecesFromChunks = 256;
+// Each piece is about kPieceGrowth times as long as the one before, so that
+// less of the prep runs alone: the prep of piece p + 1 beside the scan of
+// piece p takes about 1.0 us per 27B-shaped chunk against the scan's 1.3 us
+// (at 256 chunks, 119 + 137 chunks: 374.3 us per call against 376.0 us for
+// 128 + 128; growth 1.07: 375.2 us, 1.25: 376.0 us).  Every piece but the
+// last is a multiple of 8 chunks: the prep deals its blocks to the eight XCDs
+// by block index, key head by key head, so with a multiple of 8 chunks all
+// key heads of a chunk share one XCD and its L2 holds the gate lines they
+// share; 119 + 137 fetched 60 MB more per call.
+constexpr double kPieceGrowth = 1.15;
 
 // The second stream and the events ordering it against the caller's stream:
 // one set per device, created on first use and kept until the process ends.
@@ -665,13 +675,19 @@ SideStream* side_stream(int dev) {
 // for packed batches, checkpoints, calls whose scan already has more than one
 // workgroup per compute unit (no room beside it) and streams under graph
 // capture.  GDN_PREFILL_PIECES=n in the environment sets the count (1 to
-// kMaxPieces, each piece at least kMinPieceChunks chunks) for comparisons.
+// kMaxPieces, the first piece at least kMinPieceChunks chunks) for
+// comparisons.
 int piece_count(const PrefillArgs& a, int NTc, int scan_blocks, hipStream_t stream) {
     if (a.cu || a.ckpt || scan_blocks > 256) return 1;
     int want = NTc >= kPiecesFromChunks ? 2 : 1;
     if (const char* e = getenv("GDN_PREFILL_PIECES")) want = atoi(e);
     want = want < 1 ? 1 : (want > kMaxPieces ? kMaxPieces : want);
-    while (want > 1 && NTc / want < kMinPieceChunks) --want;
+    auto weight = [](int n) {   // sum of the relative piece lengths
+        double w = 1.0, sum = 0.0;
+        for (int p = 0; p < n; ++p, w *= kPieceGrowth) sum += w;
+        return sum;
+    };
+    while (want > 1 && NTc < kMinPieceChunks * weight(want)) --want;   // first piece too short
     if (want == 1) return 1;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
@@ -728,10 +744,17 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
         if (err != hipSuccess) return err;
         return launch_scan(a, NTc, ws, a.h0, a.hT, 0, NTc, stream);
     }
-    // pieces of whole chunks, the first ones one chunk longer
+    // pieces of whole chunks growing by kPieceGrowth, the last one taking the rest
     int first[kMaxPieces + 1];
     first[0] = 0;
-    for (int p = 0; p < P; ++p) first[p + 1] = first[p] + NTc / P + (p < NTc % P ? 1 : 0);
+    {
+        double wsum = 0.0, w = 1.0;
+        for (int p = 0; p < P; ++p, w *= kPieceGrowth) wsum += w;
+        w = 1.0;
+        for (int p = 0; p < P - 1; ++p, w *= kPieceGrowth)
+            first[p + 1] = first[p] + 8 * (int)(NTc * w / wsum / 8 + 0.5);
+        first[P] = NTc;
+    }
     float* carry = reinterpret_cast<float*>(ws + records_bytes(a.B, a.T, a.Hv));
     hipError_t err = launch_prep(a, NTc, ws, 0, first[1], stream);
     if (err == hipSuccess) err = hipEventRecord(side->start, stream);
