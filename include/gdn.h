@@ -101,8 +101,9 @@ typedef struct {
  * pass works through the first piece.  The caller's
  * stream waits for it before the call's last kernel, so for the caller the
  * call is ordered on its stream as one launch is, and the results are
- * bitwise those of one launch.  A stream under graph capture always gets one
- * piece, on the caller's stream only.  GDN_PREFILL_PIECES=n in the
+ * bitwise those of one launch.  A stream under graph capture, or one that
+ * does not belong to the current device, always gets one piece, on the
+ * caller's stream only.  GDN_PREFILL_PIECES=n in the
  * environment sets the piece count (1 to 4) for comparisons.
  */
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* problem);

@@ -736,8 +736,14 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
     SideStream* side = nullptr;
     if (P > 1) {
         lock.lock();
+        // the second stream lives on the current device: only a caller's
+        // stream on that device may hand work to it
         int dev = -1;
-        if (hipGetDevice(&dev) == hipSuccess) side = side_stream(dev);
+        hipDevice_t sdev = -1;
+        if (hipGetDevice(&dev) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess)
+            (void)hipGetLastError();   // the call goes on as one launch
+        else if (sdev == dev)
+            side = side_stream(dev);
     }
     if (!side) {
         const hipError_t err = launch_prep(a, NTc, ws, 0, NTc, stream);
