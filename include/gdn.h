@@ -20,7 +20,10 @@
  *
  * Conventions shared by every entry point
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
- *    library allocates no device memory and keeps no mutable global state.
+ *    library allocates no device memory.  Its only global state is a second
+ *    stream with its events per device, created by the first prefill call
+ *    that runs in two pieces (gdn_chunk_prefill_workspace_bytes) and kept
+ *    until the process ends.
  *  - Tensors are dense, row-major, innermost dimension last, exactly as listed;
  *    no strides.  Every pointer must be 16-byte aligned.
  *  - q, k, v and o share one storage dtype (gdn_problem.dtype).  log_g, beta

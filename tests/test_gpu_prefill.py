@@ -250,13 +250,14 @@ PIECE_T = 16400
 
 
 @pytest.mark.parametrize("case", ["plain", "zero_state", "in_place", "no_final_state",
-                                  "raw_gates", "three_pieces", "four_pieces"])
+                                  "raw_gates", "three_pieces", "four_pieces", "batch_gqa"])
 def test_pieces_bitwise_one_launch(monkeypatch, case):
     """A long call run in pieces gives bitwise the o and hT of one launch
     (GDN_PREFILL_PIECES=1), whatever the state arguments or the gate form."""
     torch = torch_mod()
-    B, Hk, Hv, d = 1, 1, 2, 128
-    say(f"pieces {case} T={PIECE_T}")
+    # two sequences of three value heads per key head: 48 scan workgroups
+    B, Hk, Hv, d = (2, 2, 6, 128) if case == "batch_gqa" else (1, 1, 2, 128)
+    say(f"pieces {case} B={B} {Hk}x{Hv} T={PIECE_T}")
     inp = gi.custom_prefill(B, PIECE_T, Hk, Hv, d, d, seed=77, dtype="bf16", gate="qwen",
                             h0="normal")
     q, k, v = dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16")
