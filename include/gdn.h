@@ -96,18 +96,19 @@ typedef struct {
  * state per (sequence, value head), handed between the two pieces of a long
  * call (next paragraph).
  *
- * On that path a call of at least 256 chunks on few sequences (no cu_seqlens,
- * no checkpoints, at most 256 scan workgroups of 32 state columns) runs as two
- * pieces of whole chunks (the second 1.15 times as long as the first): the
- * state-independent part of the second piece runs on a second stream, which
- * the library creates per device on first use and keeps, while the serial
- * pass works through the first piece.  The caller's
- * stream waits for it before the call's last kernel, so for the caller the
- * call is ordered on its stream as one launch is, and the results are
- * bitwise those of one launch.  A stream under graph capture, or one that
- * does not belong to the current device, always gets one piece, on the
- * caller's stream only.  GDN_PREFILL_PIECES=n in the
- * environment sets the piece count (1 to 4) for comparisons.
+ * On that path a call of at least 256 chunks on few sequences (no
+ * cu_seqlens, no checkpoints, and at least 4 compute units per sequence and
+ * key head left free by the B x Hv x 4 scan workgroups, one per unit) runs as
+ * two pieces of whole chunks (the second 1.15 times as long as the first):
+ * the state-independent part of the second piece runs on a second stream,
+ * which the library creates per device on first use and keeps, while the
+ * serial pass works through the first piece.  The caller's stream waits for
+ * it before the call's last kernel, so for the caller the call is ordered on
+ * its stream as one launch is, and the results are bitwise those of one
+ * launch.  A stream under graph capture, or one that does not belong to the
+ * current device, always gets one piece, on the caller's stream only.
+ * GDN_PREFILL_PIECES=n in the environment sets the piece count (1 to 4) for
+ * comparisons.
  */
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* problem);
 

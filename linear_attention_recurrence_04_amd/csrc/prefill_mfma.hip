@@ -632,6 +632,15 @@ constexpr int kPiecesFromChunks = 256;
 // key heads of a chunk share one XCD and its L2 holds the gate lines they
 // share; 119 + 137 fetched 60 MB more per call.
 constexpr double kPieceGrowth = 1.15;
+// The prep beside a scan piece runs only on the compute units the scan leaves
+// free (a scan workgroup fills its unit's LDS), so pieces need enough of
+// them: at least kFreeCUsPerRow per key-head row (sequence x key head) of
+// the prep.  The 27B shape (16 rows, 192 scan workgroups, 64 free units on
+// MI355X) is at this bound, with the second prep finishing ~13 us before
+// the first scan piece.  Below it two pieces lose: 16 key / 64 value heads
+// (256 scan workgroups, no unit free) 430 us against 409 us in one launch,
+// 5 sequences of 4 / 12 heads (240 workgroups) 537 against 515 us.
+constexpr int kFreeCUsPerRow = 4;
 
 // The second stream and the events ordering it against the caller's stream:
 // one set per device, created on first use and kept until the process ends.
@@ -645,6 +654,7 @@ struct SideStream {
     hipStream_t stream = nullptr;
     hipEvent_t start = nullptr;              // prep of piece 0 done
     hipEvent_t done[kMaxPieces] = {};        // prep of piece p done
+    int cus = 0;                             // compute units of the device
 };
 constexpr int kMaxDevices = 64;
 std::mutex side_mutex;                       // held while a call enqueues its pieces
@@ -665,6 +675,8 @@ SideStream* side_stream(int dev) {
         ok = ok && hipEventCreateWithFlags(&ss.start, flags) == hipSuccess;
         for (int p = 0; p < kMaxPieces; ++p)
             ok = ok && hipEventCreateWithFlags(&ss.done[p], flags) == hipSuccess;
+        ok = ok && hipDeviceGetAttribute(&ss.cus, hipDeviceAttributeMultiprocessorCount, dev) ==
+                       hipSuccess;
         if (!ok) (void)hipGetLastError();   // the call goes on as one piece
         ss.ok = ok;
     }
@@ -744,6 +756,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
             (void)hipGetLastError();   // the call goes on as one launch
         else if (sdev == dev)
             side = side_stream(dev);
+        if (side && side->cus - scan_blocks < kFreeCUsPerRow * a.B * a.Hk) side = nullptr;
     }
     if (!side) {
         const hipError_t err = launch_prep(a, NTc, ws, 0, NTc, stream);
