@@ -97,7 +97,7 @@ typedef struct {
  * call (next paragraph).
  *
  * On that path a call of at least 256 chunks on few sequences (no
- * cu_seqlens, no checkpoints, and at least 4 compute units per sequence and
+ * cu_seqlens, and at least 4 compute units per sequence and
  * key head left free by the B x Hv x 4 scan workgroups, one per unit) runs as
  * two pieces of whole chunks (the second 1.15 times as long as the first):
  * the state-independent part of the second piece runs on a second stream,

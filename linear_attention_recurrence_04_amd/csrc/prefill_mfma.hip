@@ -157,8 +157,8 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     int Tb;       // its length (T for equal-length batches)
     seq_span(cu, b, T, total, tb0, Tb);
     // The launch runs chunks [c_first, c_first + n_chunks) of each sequence,
-    // from the state h0 holds before chunk c_first (checkpoints need the
-    // whole sequence: c_first = 0 with them).
+    // from the state h0 holds before chunk c_first.
+    const int Tseq = Tb;                 // the whole sequence (checkpoint slots)
     const int skip = min(c_first * C, Tb);
     tb0 += skip;
     Tb = min(Tb - skip, n_chunks * C);
@@ -471,8 +471,8 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 // ---- checkpoint slot: the state after every ckpt_every tokens
                 //      and after the last token
                 if (ckpt) {
-                    const int done = min((c + 1) * C, Tb);
-                    if (done % ckpt_every == 0 || c == NTb - 1) {
+                    const int done = skip + min((c + 1) * C, Tb);   // tokens of the sequence
+                    if (done % ckpt_every == 0 || done == Tseq) {
                         const int slot = (done + ckpt_every - 1) / ckpt_every - 1;
                         float* cp = ckpt + (((size_t)b * nck + slot) * Hv + h) * D * D + jw + n;
 #pragma unroll
@@ -684,13 +684,13 @@ SideStream* side_stream(int dev) {
 }
 
 // Pieces for this call: 2 from kPiecesFromChunks chunks on, else 1; always 1
-// for packed batches, checkpoints, calls whose scan already has more than one
+// for packed batches, calls whose scan already has more than one
 // workgroup per compute unit (no room beside it) and streams under graph
 // capture.  GDN_PREFILL_PIECES=n in the environment sets the count (1 to
 // kMaxPieces, the first piece at least kMinPieceChunks chunks) for
 // comparisons.
 int piece_count(const PrefillArgs& a, int NTc, int scan_blocks, hipStream_t stream) {
-    if (a.cu || a.ckpt || scan_blocks > 256) return 1;
+    if (a.cu || scan_blocks > 256) return 1;
     int want = NTc >= kPiecesFromChunks ? 2 : 1;
     if (const char* e = getenv("GDN_PREFILL_PIECES")) want = atoi(e);
     want = want < 1 ? 1 : (want > kMaxPieces ? kMaxPieces : want);

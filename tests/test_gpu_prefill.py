@@ -347,3 +347,26 @@ def test_pieces_from_two_threads_on_two_streams():
     for i in range(2):
         for r in range(reps):
             assert torch.equal(outs[i][r], ref[i][0]) and torch.equal(hts[i][r], ref[i][1]), (i, r)
+
+
+def test_pieces_with_checkpoints_bitwise_one_launch(monkeypatch):
+    """Checkpoint slots of a long call in two pieces are bitwise those of one
+    launch, with a slot (every 448 tokens = 7 chunks) straddling the piece
+    boundary and a last, partial slot."""
+    torch = torch_mod()
+    B, Hk, Hv, d, every = 1, 1, 2, 128, 448
+    inp = gi.custom_prefill(B, PIECE_T, Hk, Hv, d, d, seed=81, dtype="bf16", gate="qwen",
+                            h0="normal")
+    q, k, v = dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16")
+    lg, bt, h0 = dev32(inp["log_g"]), dev32(inp["beta"]), dev32(inp["h0"])
+    res = {}
+    for pieces in ("1", "2"):
+        monkeypatch.setenv("GDN_PREFILL_PIECES", pieces)
+        res[pieces] = gdn.gdn_chunk_prefill_ckpt(q, k, v, lg, bt, h0, ckpt_every=every)
+        torch.cuda.synchronize()
+    monkeypatch.delenv("GDN_PREFILL_PIECES")
+    (o1, h1, c1), (o2, h2, c2) = res["1"], res["2"]
+    assert c1.shape[1] == -(-PIECE_T // every)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    assert torch.equal(c1, c2)
+    assert torch.equal(c2[:, -1], h2)   # the last slot is the final state
