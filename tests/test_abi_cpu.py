@@ -100,6 +100,18 @@ def test_workspace_query():
     assert B.gdn_chunk_prefill_workspace_bytes(P(Hv=3)) == 0   # invalid -> 0 as documented
 
 
+@pytest.mark.parametrize("Bn,T,Hk,Hv", [(1, 1, 1, 1), (2, 200, 1, 3), (1, 16384, 16, 48),
+                                        (3, 16400, 2, 6)])
+def test_mfma_workspace_bytes_as_documented(Bn, T, Hk, Hv):
+    """bf16, d = 128, chunk 64 takes the MFMA path, whose workspace is 13568
+    bytes per (sequence, value head, chunk of 64) plus one fp32 state per
+    (sequence, value head) for the hand-over between the pieces of a long call."""
+    prob = P(B=Bn, T=T, Hk=Hk, Hv=Hv, dk=128, dv=128, chunk=64, dtype=1)
+    assert B.gdn_chunk_prefill_variant(prob) == "mfma_bf16"
+    chunks = -(-T // 64)
+    assert B.gdn_chunk_prefill_workspace_bytes(prob) == Bn * Hv * (chunks * 13568 + 128 * 128 * 4)
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 4, 1, 64)
