@@ -20,10 +20,9 @@
  *
  * Conventions shared by every entry point
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
- *    library allocates no device memory.  Its only global state is a second
- *    stream with its events per device, created by the first prefill call
- *    that runs in two pieces (gdn_chunk_prefill_workspace_bytes) and kept
- *    until the process ends.
+ *    library allocates no memory, creates no stream or event and keeps no
+ *    global state: a call enqueues kernels on the caller's stream only, so
+ *    calls on different streams never wait on one another.
  *  - Tensors are dense, row-major, innermost dimension last, exactly as listed;
  *    no strides.  Every pointer must be 16-byte aligned.
  *  - q, k, v and o share one storage dtype (gdn_problem.dtype).  log_g, beta
@@ -92,23 +91,7 @@ typedef struct {
  * initialisation and are meaningless after the call.  The bf16 MFMA path
  * ("mfma_bf16" below) needs 13568 bytes per (sequence, value head, chunk of
  * 64 tokens): the chunk's triangular inverse, masked Q K^T and gate vectors,
- * computed for all chunks in parallel before the serial pass; plus one fp32
- * state per (sequence, value head), handed between the two pieces of a long
- * call (next paragraph).
- *
- * On that path a call of at least 256 chunks on few sequences (no
- * cu_seqlens, and at least 4 compute units per sequence and
- * key head left free by the B x Hv x 4 scan workgroups, one per unit) runs as
- * two pieces of whole chunks (the second 1.15 times as long as the first):
- * the state-independent part of the second piece runs on a second stream,
- * which the library creates per device on first use and keeps, while the
- * serial pass works through the first piece.  The caller's stream waits for
- * it before the call's last kernel, so for the caller the call is ordered on
- * its stream as one launch is, and the results are bitwise those of one
- * launch.  A stream under graph capture, or one that does not belong to the
- * current device, always gets one piece, on the caller's stream only.
- * GDN_PREFILL_PIECES=n in the environment sets the piece count (1 to 4) for
- * comparisons.
+ * computed for all chunks in parallel before the serial pass.
  */
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* problem);
 

@@ -9,6 +9,7 @@ a missing library raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Tuple
 
@@ -165,6 +166,22 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
+def _on_stream(fn):
+    """Run a wrapper with ``stream`` (when given) as torch's current stream, so
+    that every tensor it allocates (outputs, workspace) belongs to the stream
+    the kernels run on: the caching allocator then reuses such memory only
+    for work ordered after those kernels, also once the wrapper's local
+    workspace is released."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, **kwargs)
+        with _torch().cuda.stream(stream):
+            return fn(*args, stream=stream, **kwargs)
+    return wrapper
+
+
+@_on_stream
 def gdn_chunk_prefill(q, k, v, log_g, beta, h0=None, *, chunk: int = 64,
                       qk_l2norm: bool = True, q_scale: float = 1.0, out=None, hT=None,
                       want_state: bool = True, workspace=None,
@@ -204,6 +221,7 @@ def gdn_chunk_prefill(q, k, v, log_g, beta, h0=None, *, chunk: int = 64,
     return out, hT
 
 
+@_on_stream
 def gdn_chunk_prefill_ckpt(q, k, v, log_g, beta, h0=None, *, ckpt_every: int,
                            chunk: int = 64, qk_l2norm: bool = True, q_scale: float = 1.0,
                            out=None, hT=None, h_ckpt=None, workspace=None, stream=None):
@@ -249,6 +267,7 @@ def gdn_chunk_prefill_ckpt(q, k, v, log_g, beta, h0=None, *, ckpt_every: int,
     return out, hT, h_ckpt
 
 
+@_on_stream
 def gdn_decode_step(q, k, v, log_g, beta, state, *, qk_l2norm: bool = True,
                     q_scale: float = 1.0, out=None, stream=None):
     """One decode step.  q, k [B,Hk,d]; v [B,Hv,d]; log_g, beta [B,Hv] fp32;
@@ -275,6 +294,7 @@ def gdn_decode_step(q, k, v, log_g, beta, state, *, qk_l2norm: bool = True,
     return out
 
 
+@_on_stream
 def gdn_chunk_prefill_gated(q, k, v, a, b, A_log, dt_bias, h0=None, *, ckpt_every: int = 0,
                             chunk: int = 64, qk_l2norm: bool = True, q_scale: float = 1.0,
                             out=None, hT=None, h_ckpt=None, workspace=None, stream=None):
@@ -326,6 +346,7 @@ def gdn_chunk_prefill_gated(q, k, v, a, b, A_log, dt_bias, h0=None, *, ckpt_ever
     return out, hT, (h_ckpt if every > 0 else None)
 
 
+@_on_stream
 def gdn_decode_step_gated(q, k, v, a, b, A_log, dt_bias, state, *, qk_l2norm: bool = True,
                           q_scale: float = 1.0, out=None, stream=None):
     """One decode step with the gates formed in the kernel from a, b [B,Hv] fp32
@@ -355,6 +376,7 @@ def gdn_decode_step_gated(q, k, v, a, b, A_log, dt_bias, state, *, qk_l2norm: bo
     return out
 
 
+@_on_stream
 def gdn_decode_multi(q, k, v, log_g, beta, state, *, A_log=None, dt_bias=None,
                      want_states: bool = False, qk_l2norm: bool = True, q_scale: float = 1.0,
                      out=None, states=None, stream=None):
@@ -395,6 +417,7 @@ def gdn_decode_multi(q, k, v, log_g, beta, state, *, A_log=None, dt_bias=None,
     return out, states
 
 
+@_on_stream
 def gdn_chunk_prefill_varlen(q, k, v, log_g, beta, cu_seqlens, max_seqlen: Optional[int] = None,
                              h0=None, *, chunk: int = 64, qk_l2norm: bool = True,
                              q_scale: float = 1.0, out=None, hT=None, workspace=None,

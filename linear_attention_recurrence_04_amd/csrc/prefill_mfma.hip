@@ -42,9 +42,6 @@
 //    global -> LDS loads.
 #include "prefill_mfma_common.h"
 
-#include <cstdlib>
-#include <mutex>
-
 namespace gdn {
 namespace mfma_prefill {
 
@@ -592,121 +589,10 @@ namespace {
 
 using namespace mfma_prefill;
 
-// Records of every (b, value head, chunk), then the fp32 state handed from
-// one piece of a call to the next (below).
+// Records of every (b, value head, chunk).
 size_t records_bytes(int B, int T, int Hv) {
     const size_t NTc = (size_t)(T + C - 1) / C;
     return (size_t)B * Hv * NTc * WS_REC;
-}
-
-// A long call on few sequences runs as up to kMaxPieces pieces of whole
-// chunks.  The prep of piece 0 runs first, on the caller's stream; the preps
-// of the later pieces run in order on a second stream owned by the library,
-// and the scan of piece p, on the caller's stream, waits only for the prep of
-// piece p and starts from the fp32 state the scan of piece p - 1 left in the
-// workspace.  The preps of later pieces so run beside the scan of earlier
-// ones, on the compute units the scan leaves free.  The pieces compute
-// exactly what one launch computes: each chunk's records and its step of the
-// chain are the same, and the state passes between pieces unrounded.
-//
-// A scan workgroup holds nearly all of a compute unit's LDS, so a prep
-// workgroup runs only on a unit the scan leaves free.  Measured on MI355X
-// (bf16, head dim 128, one sequence, per call): two pieces take 16 key / 48
-// value heads from 395 to 380 us at T = 16384 and from 776 to 726 us at
-// T = 32768; at T = 8192 they break even and at T = 4096 or 2048 they lose
-// 5 to 11 us (the hand-over between the streams).  Three or four pieces are
-// slower than two at every size tried: at each piece boundary where a later
-// prep is still queued, that prep takes the units the finishing scan frees
-// and the next scan piece waits for them.  Hence two pieces from
-// kPiecesFromChunks chunks on.
-constexpr int kMaxPieces = 4;
-constexpr int kMinPieceChunks = 16;
-constexpr int kPiecesFromChunks = 256;
-// Each piece is about kPieceGrowth times as long as the one before, so that
-// less of the prep runs alone: the prep of piece p + 1 beside the scan of
-// piece p takes about 1.0 us per 27B-shaped chunk against the scan's 1.3 us
-// (at 256 chunks, 119 + 137 chunks: 374.3 us per call against 376.0 us for
-// 128 + 128; growth 1.07: 375.2 us, 1.25: 376.0 us).  Every piece but the
-// last is a multiple of 8 chunks: the prep deals its blocks to the eight XCDs
-// by block index, key head by key head, so with a multiple of 8 chunks all
-// key heads of a chunk share one XCD and its L2 holds the gate lines they
-// share; 119 + 137 fetched 60 MB more per call.
-constexpr double kPieceGrowth = 1.15;
-// The prep beside a scan piece runs only on the compute units the scan leaves
-// free (a scan workgroup fills its unit's LDS), so pieces need enough of
-// them: at least kFreeCUsPerRow per key-head row (sequence x key head) of
-// the prep.  The 27B shape (16 rows, 192 scan workgroups, 64 free units on
-// MI355X) is at this bound, with the second prep finishing ~13 us before
-// the first scan piece.  Below it two pieces lose: 16 key / 64 value heads
-// (256 scan workgroups, no unit free) 430 us against 409 us in one launch,
-// 5 sequences of 4 / 12 heads (240 workgroups) 537 against 515 us.
-constexpr int kFreeCUsPerRow = 4;
-
-// The second stream and the events ordering it against the caller's stream:
-// one set per device, created on first use and kept until the process ends.
-// Default priority and no blocking against the legacy null stream.  Calls on
-// different streams of a device share it, so the second piece of one call may
-// wait behind that of a call enqueued before it (never on a later one: every
-// wait is on work enqueued earlier, so no cycle can form).
-struct SideStream {
-    bool tried = false;
-    bool ok = false;
-    hipStream_t stream = nullptr;
-    hipEvent_t start = nullptr;              // prep of piece 0 done
-    hipEvent_t done[kMaxPieces] = {};        // prep of piece p done
-    int cus = 0;                             // compute units of the device
-};
-constexpr int kMaxDevices = 64;
-std::mutex side_mutex;                       // held while a call enqueues its pieces
-SideStream side_streams[kMaxDevices];
-
-// The current device's side stream, or nullptr when it cannot be had (called
-// with side_mutex held).
-SideStream* side_stream(int dev) {
-    if (dev < 0 || dev >= kMaxDevices) return nullptr;
-    SideStream& ss = side_streams[dev];
-    if (!ss.tried) {
-        ss.tried = true;
-        // Both streams are on one device and nothing is read by the host, so
-        // the events need device-scope fences only; the default system-scope
-        // fence measured 10 us of idle time per hand-over.
-        const unsigned flags = hipEventDisableTiming | hipEventDisableSystemFence;
-        bool ok = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) == hipSuccess;
-        ok = ok && hipEventCreateWithFlags(&ss.start, flags) == hipSuccess;
-        for (int p = 0; p < kMaxPieces; ++p)
-            ok = ok && hipEventCreateWithFlags(&ss.done[p], flags) == hipSuccess;
-        ok = ok && hipDeviceGetAttribute(&ss.cus, hipDeviceAttributeMultiprocessorCount, dev) ==
-                       hipSuccess;
-        if (!ok) (void)hipGetLastError();   // the call goes on as one piece
-        ss.ok = ok;
-    }
-    return ss.ok ? &ss : nullptr;
-}
-
-// Pieces for this call: 2 from kPiecesFromChunks chunks on, else 1; always 1
-// for packed batches, calls whose scan already has more than one
-// workgroup per compute unit (no room beside it) and streams under graph
-// capture.  GDN_PREFILL_PIECES=n in the environment sets the count (1 to
-// kMaxPieces, the first piece at least kMinPieceChunks chunks) for
-// comparisons.
-int piece_count(const PrefillArgs& a, int NTc, int scan_blocks, hipStream_t stream) {
-    if (a.cu || scan_blocks > 256) return 1;
-    int want = NTc >= kPiecesFromChunks ? 2 : 1;
-    if (const char* e = getenv("GDN_PREFILL_PIECES")) want = atoi(e);
-    want = want < 1 ? 1 : (want > kMaxPieces ? kMaxPieces : want);
-    auto weight = [](int n) {   // sum of the relative piece lengths
-        double w = 1.0, sum = 0.0;
-        for (int p = 0; p < n; ++p, w *= kPieceGrowth) sum += w;
-        return sum;
-    };
-    while (want > 1 && NTc < kMinPieceChunks * weight(want)) --want;   // first piece too short
-    if (want == 1) return 1;
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
-        (void)hipGetLastError();
-        return 1;
-    }
-    return cap == hipStreamCaptureStatusNone ? want : 1;
 }
 
 hipError_t launch_prep(const PrefillArgs& a, int NTc, unsigned char* ws, int c_first,
@@ -735,60 +621,17 @@ hipError_t launch_scan(const PrefillArgs& a, int NTc, const unsigned char* ws, c
 
 size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv) {
     (void)Hk;
-    return records_bytes(B, T, Hv) + (size_t)B * Hv * D * D * sizeof(float);
+    return records_bytes(B, T, Hv);
 }
 
+// The prep of every chunk, then the serial pass, both on the caller's stream.
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
     const int NTc = (a.T + C - 1) / C;
     if (a.B * a.Hk * NTc == 0) return hipSuccess;
     unsigned char* ws = static_cast<unsigned char*>(a.ws);
-    const int scan_blocks = a.B * a.Hv * (D / BVS);
-    const int P = piece_count(a, NTc, scan_blocks, stream);
-    std::unique_lock<std::mutex> lock(side_mutex, std::defer_lock);
-    SideStream* side = nullptr;
-    if (P > 1) {
-        lock.lock();
-        // the second stream lives on the current device: only a caller's
-        // stream on that device may hand work to it
-        int dev = -1;
-        hipDevice_t sdev = -1;
-        if (hipGetDevice(&dev) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess)
-            (void)hipGetLastError();   // the call goes on as one launch
-        else if (sdev == dev)
-            side = side_stream(dev);
-        if (side && side->cus - scan_blocks < kFreeCUsPerRow * a.B * a.Hk) side = nullptr;
-    }
-    if (!side) {
-        const hipError_t err = launch_prep(a, NTc, ws, 0, NTc, stream);
-        if (err != hipSuccess) return err;
-        return launch_scan(a, NTc, ws, a.h0, a.hT, 0, NTc, stream);
-    }
-    // pieces of whole chunks growing by kPieceGrowth, the last one taking the rest
-    int first[kMaxPieces + 1];
-    first[0] = 0;
-    {
-        double wsum = 0.0, w = 1.0;
-        for (int p = 0; p < P; ++p, w *= kPieceGrowth) wsum += w;
-        w = 1.0;
-        for (int p = 0; p < P - 1; ++p, w *= kPieceGrowth)
-            first[p + 1] = first[p] + 8 * (int)(NTc * w / wsum / 8 + 0.5);
-        first[P] = NTc;
-    }
-    float* carry = reinterpret_cast<float*>(ws + records_bytes(a.B, a.T, a.Hv));
-    hipError_t err = launch_prep(a, NTc, ws, 0, first[1], stream);
-    if (err == hipSuccess) err = hipEventRecord(side->start, stream);
-    if (err == hipSuccess) err = hipStreamWaitEvent(side->stream, side->start, 0);
-    for (int p = 1; p < P && err == hipSuccess; ++p) {
-        err = launch_prep(a, NTc, ws, first[p], first[p + 1] - first[p], side->stream);
-        if (err == hipSuccess) err = hipEventRecord(side->done[p], side->stream);
-    }
-    for (int p = 0; p < P && err == hipSuccess; ++p) {
-        if (p > 0) err = hipStreamWaitEvent(stream, side->done[p], 0);
-        if (err == hipSuccess)
-            err = launch_scan(a, NTc, ws, p == 0 ? a.h0 : carry, p == P - 1 ? a.hT : carry,
-                              first[p], first[p + 1] - first[p], stream);
-    }
-    return err;
+    const hipError_t err = launch_prep(a, NTc, ws, 0, NTc, stream);
+    if (err != hipSuccess) return err;
+    return launch_scan(a, NTc, ws, a.h0, a.hT, 0, NTc, stream);
 }
 
 }  // namespace gdn

@@ -104,12 +104,11 @@ def test_workspace_query():
                                         (3, 16400, 2, 6)])
 def test_mfma_workspace_bytes_as_documented(Bn, T, Hk, Hv):
     """bf16, d = 128, chunk 64 takes the MFMA path, whose workspace is 13568
-    bytes per (sequence, value head, chunk of 64) plus one fp32 state per
-    (sequence, value head) for the hand-over between the pieces of a long call."""
+    bytes per (sequence, value head, chunk of 64)."""
     prob = P(B=Bn, T=T, Hk=Hk, Hv=Hv, dk=128, dv=128, chunk=64, dtype=1)
     assert B.gdn_chunk_prefill_variant(prob) == "mfma_bf16"
     chunks = -(-T // 64)
-    assert B.gdn_chunk_prefill_workspace_bytes(prob) == Bn * Hv * (chunks * 13568 + 128 * 128 * 4)
+    assert B.gdn_chunk_prefill_workspace_bytes(prob) == Bn * Hv * chunks * 13568
 
 
 def test_python_binding_refuses_cpu_tensors():

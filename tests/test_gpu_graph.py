@@ -1,9 +1,8 @@
 """Library calls captured into a HIP graph (torch.cuda.graph) and replayed:
 every replay, with eager work and synchronisation between replays, must give
 bitwise the eager result.  Under capture the library enqueues only kernels
-on the caller's stream (no allocation, no memset, no synchronisation, and a
-long prefill that runs eagerly as two pieces on two streams runs as one
-piece), which is what makes its calls capturable."""
+on the caller's stream (no allocation, no memset, no synchronisation), which
+is what makes its calls capturable."""
 import numpy as np
 import pytest
 
@@ -52,7 +51,7 @@ def test_decode_steps_in_a_graph():
         assert torch.equal(out, o_ref) and torch.equal(state, s_ref), f"replay {rep}"
 
 
-# T = 16400 is 257 chunks of 64: two pieces eagerly, one under capture
+# T = 16400 is 257 chunks of 64, the last one ragged
 @pytest.mark.parametrize("dtype,d,C,T", [("bf16", 128, 64, 200), ("f32", 64, 32, 200),
                                          ("bf16", 128, 64, 16400)])
 def test_prefill_in_a_graph(dtype, d, C, T):

@@ -244,80 +244,37 @@ def test_mfma_gqa_ratios(Hk, Hv):
     assert_parity(host(o), o_ref, host(hT), h_ref, "bf16", f"mfma {Hk}x{Hv}")
 
 
-# 16400 tokens = 257 chunks of 64 (last one ragged): a call this long runs as
-# two pieces (129 + 128 chunks) with the second piece's prep on a second stream
-PIECE_T = 16400
+# 16400 tokens = 257 chunks of 64, the last one ragged
+LONG_T = 16400
 
 
-@pytest.mark.parametrize("case", ["plain", "zero_state", "in_place", "no_final_state",
-                                  "raw_gates", "three_pieces", "four_pieces", "batch_gqa"])
-def test_pieces_bitwise_one_launch(monkeypatch, case):
-    """A long call run in pieces gives bitwise the o and hT of one launch
-    (GDN_PREFILL_PIECES=1), whatever the state arguments or the gate form."""
-    torch = torch_mod()
-    # two sequences of three value heads per key head: 48 scan workgroups
-    B, Hk, Hv, d = (2, 2, 6, 128) if case == "batch_gqa" else (1, 1, 2, 128)
-    say(f"pieces {case} B={B} {Hk}x{Hv} T={PIECE_T}")
-    inp = gi.custom_prefill(B, PIECE_T, Hk, Hv, d, d, seed=77, dtype="bf16", gate="qwen",
-                            h0="normal")
-    q, k, v = dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16")
-    lg, bt = dev32(inp["log_g"]), dev32(inp["beta"])
-    raw = gi.make_raw_gates((B, PIECE_T), Hv, seed=78) if case == "raw_gates" else None
-    pieces = {"three_pieces": "3", "four_pieces": "4"}.get(case, "2")
-
-    def call():
-        h0 = None if case == "zero_state" else dev32(inp["h0"])
-        if raw is not None:
-            o, hT, _ = gdn.gdn_chunk_prefill_gated(q, k, v, dev32(raw["a"]), dev32(raw["b"]),
-                                                   dev32(raw["A_log"]), dev32(raw["dt_bias"]), h0)
-        elif case == "in_place":
-            o, hT = gdn.gdn_chunk_prefill(q, k, v, lg, bt, h0, hT=h0)
-            assert hT is h0
-        else:
-            o, hT = gdn.gdn_chunk_prefill(q, k, v, lg, bt, h0,
-                                          want_state=case != "no_final_state")
-        torch.cuda.synchronize()
-        return o, hT
-
-    monkeypatch.setenv("GDN_PREFILL_PIECES", "1")
-    o1, h1 = call()
-    monkeypatch.setenv("GDN_PREFILL_PIECES", pieces)
-    o2, h2 = call()
-    monkeypatch.delenv("GDN_PREFILL_PIECES")
-    assert torch.equal(o1, o2), case
-    if case == "no_final_state":
-        assert h1 is None and h2 is None
-    else:
-        assert torch.equal(h1, h2), case
-
-
-def test_two_pieces_match_oracle():
-    """The default two-piece path on a long ragged call, against the oracle."""
-    inp = gi.custom_prefill(1, PIECE_T, 1, 2, 128, 128, seed=79, dtype="bf16", gate="qwen",
+def test_long_ragged_call_matches_oracle():
+    """A long ragged call (257 chunks) against the oracle."""
+    inp = gi.custom_prefill(1, LONG_T, 1, 2, 128, 128, seed=79, dtype="bf16", gate="qwen",
                             h0="normal")
     o, hT = run_prefill(inp, "bf16", 64)
     o_ref, h_ref = run_oracle(inp)
-    assert_parity(host(o), o_ref, host(hT), h_ref, "bf16", f"two pieces T={PIECE_T}")
+    assert_parity(host(o), o_ref, host(hT), h_ref, "bf16", f"long ragged T={LONG_T}")
 
 
-def test_pieces_from_two_threads_on_two_streams():
+def test_two_threads_on_two_streams():
     """Two host threads, each on a stream and workspace of its own, enqueue long
-    two-piece calls at the same time, so both share the library's second
-    stream; every result is bitwise that of the same call made alone."""
+    calls at the same time; every result is bitwise that of the same call made
+    alone on the current stream."""
     import threading
     torch = torch_mod()
     B, Hk, Hv, d, reps = 1, 1, 2, 128, 4
-    say(f"two threads x {reps} calls of T={PIECE_T}")
+    say(f"two threads x {reps} calls of T={LONG_T}")
     args = []
     for i in range(2):
-        inp = gi.custom_prefill(B, PIECE_T, Hk, Hv, d, d, seed=90 + i, dtype="bf16", gate="qwen",
+        inp = gi.custom_prefill(B, LONG_T, Hk, Hv, d, d, seed=90 + i, dtype="bf16", gate="qwen",
                                 h0="normal")
         a = {n: dev(inp[n], "bf16") for n in ("q", "k", "v")}
         a.update({n: dev32(inp[n]) for n in ("log_g", "beta", "h0")})
         args.append(a)
     ref = [gdn.gdn_chunk_prefill(a["q"], a["k"], a["v"], a["log_g"], a["beta"], a["h0"])
            for a in args]
-    prob = gdn.make_problem(B, PIECE_T, Hk, Hv, d, d, chunk=64, dtype=gdn.GDN_DTYPE_BF16)
+    prob = gdn.make_problem(B, LONG_T, Hk, Hv, d, d, chunk=64, dtype=gdn.GDN_DTYPE_BF16)
     ws = [torch.empty(gdn.gdn_chunk_prefill_workspace_bytes(prob), dtype=torch.uint8,
                       device="cuda") for _ in range(2)]
     outs = [[torch.empty_like(ref[i][0]) for _ in range(reps)] for i in range(2)]
@@ -349,24 +306,26 @@ def test_pieces_from_two_threads_on_two_streams():
             assert torch.equal(outs[i][r], ref[i][0]) and torch.equal(hts[i][r], ref[i][1]), (i, r)
 
 
-def test_pieces_with_checkpoints_bitwise_one_launch(monkeypatch):
-    """Checkpoint slots of a long call in two pieces are bitwise those of one
-    launch, with a slot (every 448 tokens = 7 chunks) straddling the piece
-    boundary and a last, partial slot."""
+def test_stream_argument_owns_its_allocations():
+    """stream= with no workspace or outputs passed: what the binding allocates
+    belongs to that stream, so memory taken on the current stream straight
+    after the call (and filled there at once) never lands on buffers the
+    kernels on the other stream still use; results bitwise those of the same
+    call on the current stream."""
     torch = torch_mod()
-    B, Hk, Hv, d, every = 1, 1, 2, 128, 448
-    inp = gi.custom_prefill(B, PIECE_T, Hk, Hv, d, d, seed=81, dtype="bf16", gate="qwen",
+    inp = gi.custom_prefill(1, LONG_T, 1, 3, 128, 128, seed=93, dtype="bf16", gate="qwen",
                             h0="normal")
-    q, k, v = dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16")
-    lg, bt, h0 = dev32(inp["log_g"]), dev32(inp["beta"]), dev32(inp["h0"])
-    res = {}
-    for pieces in ("1", "2"):
-        monkeypatch.setenv("GDN_PREFILL_PIECES", pieces)
-        res[pieces] = gdn.gdn_chunk_prefill_ckpt(q, k, v, lg, bt, h0, ckpt_every=every)
+    a = {n: dev(inp[n], "bf16") for n in ("q", "k", "v")}
+    a.update({n: dev32(inp[n]) for n in ("log_g", "beta", "h0")})
+    o_ref, h_ref = gdn.gdn_chunk_prefill(a["q"], a["k"], a["v"], a["log_g"], a["beta"], a["h0"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        o, hT = gdn.gdn_chunk_prefill(a["q"], a["k"], a["v"], a["log_g"], a["beta"], a["h0"],
+                                      stream=side)
+        junk = [torch.full((o_ref.numel(),), 7.0, device="cuda") for _ in range(4)]
+        side.synchronize()
         torch.cuda.synchronize()
-    monkeypatch.delenv("GDN_PREFILL_PIECES")
-    (o1, h1, c1), (o2, h2, c2) = res["1"], res["2"]
-    assert c1.shape[1] == -(-PIECE_T // every)
-    assert torch.equal(o1, o2) and torch.equal(h1, h2)
-    assert torch.equal(c1, c2)
-    assert torch.equal(c2[:, -1], h2)   # the last slot is the final state
+        assert torch.equal(o, o_ref) and torch.equal(hT, h_ref), rep
+        del junk
