@@ -92,6 +92,7 @@ typedef struct {
  * ("mfma_bf16" below) needs 13568 bytes per (sequence, value head, chunk of
  * 64 tokens): the chunk's triangular inverse, masked Q K^T and gate vectors,
  * computed for all chunks in parallel before the serial pass.
+ * gdn_chunk_prefill_onchip needs no workspace.
  */
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* problem);
 
@@ -215,6 +216,35 @@ gdn_status gdn_chunk_prefill_varlen(const gdn_problem* problem, const int32_t* c
                                     void* hip_stream);
 
 /*
+ * gdn_chunk_prefill in a single pass that keeps every per-chunk intermediate
+ * on chip: no workspace, nothing written to memory but o, hT and the
+ * checkpoint slots.  The pages' context-encoding kernels are organised the
+ * same way, the whole chunked forward with its direct triangular solve in one
+ * kernel ("Qwen3.6: Fused DeltaNet Direct-Solve Follow-Up", "Implementation
+ * Details"; "Add Qwen3.5-2B contrib model", "Description").
+ *
+ * For bf16 inputs with d = 128 and chunk 64, each workgroup owns 32 state
+ * columns of one value head and forms the chunk's gates, decay-masked
+ * K K^T, triangular inverse and masked Q K^T itself, beside the serial
+ * state update; other supported shapes run the fp32 kernel, which needs no
+ * workspace either.  Arguments, checks and results as
+ * gdn_chunk_prefill_ckpt (h_ckpt may be NULL with ckpt_every == 0 for no
+ * checkpoints).  Splitting a sequence at multiples of the chunk across calls
+ * of this entry point gives bitwise the same results; against
+ * gdn_chunk_prefill the results agree to rounding, not bitwise (different
+ * kernels, different summation orders).  gdn_chunk_prefill is the faster of
+ * the two for long calls (the per-chunk work of a value head is repeated in
+ * its four column workgroups here); this one is for callers that cannot
+ * provide a workspace and for short calls.
+ */
+gdn_status gdn_chunk_prefill_onchip(const gdn_problem* problem,
+                                    const void* q, const void* k, const void* v,
+                                    const float* log_g, const float* beta,
+                                    const float* h0, float* hT, void* o,
+                                    float* h_ckpt, int32_t ckpt_every,
+                                    void* hip_stream);
+
+/*
  * Multi-token decode: problem->T >= 0 tokens per sequence applied in order to
  * a state that stays on chip for the whole call, for speculative or
  * multi-token-prediction verification and small continuous-batching steps
@@ -290,7 +320,8 @@ gdn_status gdn_decode_step_gated(const gdn_problem* problem,
  * Name of the prefill kernel variant gdn_chunk_prefill launches for this
  * problem (static storage, never NULL): "generic_f32" (fp32 arithmetic, any
  * supported shape), "mfma_bf16" (bf16 MFMA path for bf16 inputs, d = 128,
- * chunk 64), or "invalid" when the problem would be rejected.  Pure query:
+ * chunk 64: a parallel prep kernel, then the serial scan), or "invalid" when
+ * the problem would be rejected.  Pure query:
  * enqueues nothing.  Setting GDN_FORCE_GENERIC=1 in the environment makes
  * every prefill use "generic_f32" (for A/B comparisons of the two kernels).
  */

@@ -74,6 +74,9 @@ def lib():
     L.gdn_chunk_prefill_varlen.restype = ctypes.c_int
     L.gdn_chunk_prefill_varlen.argtypes = [pp, vp, ctypes.c_int64, vp, vp, vp, fp, fp, fp, fp, vp,
                                            vp, sz, vp]
+    L.gdn_chunk_prefill_onchip.restype = ctypes.c_int
+    L.gdn_chunk_prefill_onchip.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, vp, fp, ctypes.c_int32,
+                                           vp]
     L.gdn_decode_step.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [pp, vp, vp, vp, fp, fp, fp, vp, vp]
     _lib = L
@@ -113,6 +116,10 @@ VARIANTS = {
     "mfma_bf16": ("chunk_prep_kernel+chunk_scan_kernel", "bf16-mfma",
                   ("prefill_mfma.hip", "prefill_mfma_common.h", "prefill_prep.inc", "gdn_device.h")),
 }
+
+# the single-pass kernel of gdn_chunk_prefill_onchip (bf16, d = 128, chunk 64)
+ONCHIP_KERNEL = {"name": "chunk_fused_kernel<false>", "arith": "bf16-mfma",
+                 "sources": ("prefill_fused.hip", "prefill_mfma_common.h", "gdn_device.h")}
 
 
 def selected_prefill_kernel(problem: GdnProblem) -> dict:
@@ -465,3 +472,48 @@ def gdn_chunk_prefill_varlen(q, k, v, log_g, beta, cu_seqlens, max_seqlen: Optio
                                         _stream(stream))
     _check(st)
     return out, hT
+
+
+@_on_stream
+def gdn_chunk_prefill_onchip(q, k, v, log_g, beta, h0=None, *, ckpt_every: int = 0,
+                             chunk: int = 64, qk_l2norm: bool = True, q_scale: float = 1.0,
+                             out=None, hT=None, h_ckpt=None, want_state: bool = True,
+                             stream=None):
+    """Chunked prefill in a single pass with every intermediate on chip (no
+    workspace).  Arguments as gdn_chunk_prefill_ckpt; returns (o, hT, h_ckpt),
+    h_ckpt None unless ckpt_every > 0."""
+    torch = _torch()
+    _need(q, "q")
+    dt = _dtype_code(q)
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    _need(k, "k", q.dtype, q.shape)
+    _need(v, "v", q.dtype, (B, T, Hv, dv))
+    _need(log_g, "log_g", torch.float32, (B, T, Hv))
+    _need(beta, "beta", torch.float32, (B, T, Hv))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, Hv, dk, dv))
+    every = int(ckpt_every)
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(out, "out", q.dtype, (B, T, Hv, dv))
+    if hT is None and want_state:
+        hT = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=q.device)
+    elif hT is not None:
+        _need(hT, "hT", torch.float32, (B, Hv, dk, dv))
+    ck_ptr = None
+    if every > 0:
+        nck = -(-T // every)
+        if h_ckpt is None:
+            h_ckpt = torch.empty((B, nck, Hv, dk, dv), dtype=torch.float32, device=q.device)
+        else:
+            _need(h_ckpt, "h_ckpt", torch.float32, (B, nck, Hv, dk, dv))
+        ck_ptr = _ptr(h_ckpt) if h_ckpt.numel() else None
+    prob = make_problem(B, T, Hk, Hv, dk, dv, chunk=chunk, dtype=dt, qk_l2norm=qk_l2norm,
+                        q_scale=q_scale)
+    st = lib().gdn_chunk_prefill_onchip(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(log_g), _ptr(beta), _ptr(h0), _ptr(hT), _ptr(out),
+                                        ck_ptr, every, _stream(stream))
+    _check(st)
+    return out, hT, (h_ckpt if every > 0 else None)

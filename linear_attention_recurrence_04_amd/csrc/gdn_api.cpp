@@ -74,6 +74,10 @@ bool force_generic() {
 
 bool use_mfma(const gdn::PrefillArgs& a) { return !force_generic() && gdn::prefill_mfma_supported(a); }
 
+size_t mfma_workspace_bytes(const gdn::PrefillArgs& a) {
+    return gdn::prefill_mfma_workspace_bytes(a.B, a.T, a.Hk, a.Hv);
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,7 +106,7 @@ const char* gdn_chunk_prefill_variant(const gdn_problem* p) {
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* p) {
     if (check_problem(p, false) != GDN_OK) return 0;
     const gdn::PrefillArgs a = prefill_args(p);
-    if (use_mfma(a)) return gdn::prefill_mfma_workspace_bytes(a.B, a.T, a.Hk, a.Hv);
+    if (use_mfma(a)) return mfma_workspace_bytes(a);
     return 0;  // the fp32 kernel keeps every intermediate on chip
 }
 
@@ -120,7 +124,7 @@ gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, cons
                         const float* dt_bias, const float* h0, float* hT, void* o,
                         float* h_ckpt, int ckpt_every, void* workspace,
                         size_t workspace_bytes, void* hip_stream,
-                        const int32_t* cu = nullptr, long long total = -1) {
+                        const int32_t* cu = nullptr, long long total = -1, bool onchip = false) {
     const size_t es = dsize(p);
     if (total < 0) total = (long long)p->B * p->T;
     const size_t BT = (size_t)total;
@@ -137,7 +141,7 @@ gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, cons
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
 
-    const size_t need_ws = gdn_chunk_prefill_workspace_bytes(p);
+    const size_t need_ws = onchip ? 0 : gdn_chunk_prefill_workspace_bytes(p);
     if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return GDN_ERR_WORKSPACE;
 
     // outputs against inputs: hT may be exactly h0, nothing else may overlap
@@ -178,7 +182,8 @@ gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, cons
     a.ckpt = nck > 0 ? h_ckpt : nullptr;
     a.ckpt_every = nck > 0 ? ckpt_every : 0;
     a.nck = nck;
-    err = use_mfma(a) ? gdn::launch_prefill_mfma(a, stream) : gdn::launch_prefill_generic(a, stream);
+    if (!use_mfma(a)) err = gdn::launch_prefill_generic(a, stream);
+    else err = onchip ? gdn::launch_prefill_fused(a, stream) : gdn::launch_prefill_mfma(a, stream);
     return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
@@ -236,6 +241,19 @@ gdn_status gdn_chunk_prefill_varlen(const gdn_problem* p, const int32_t* cu_seql
     if (p->B > 0 && !cu_seqlens) return GDN_ERR_NULL_POINTER;
     return prefill_impl(p, q, k, v, log_g, beta, nullptr, nullptr, h0, hT, o, nullptr, 0,
                         workspace, workspace_bytes, hip_stream, cu_seqlens, total_tokens);
+}
+
+gdn_status gdn_chunk_prefill_onchip(const gdn_problem* p, const void* q, const void* k,
+                                    const void* v, const float* log_g, const float* beta,
+                                    const float* h0, float* hT, void* o, float* h_ckpt,
+                                    int32_t ckpt_every, void* hip_stream) {
+    const gdn_status st = check_problem(p, false);
+    if (st != GDN_OK) return st;
+    const int C = p->chunk ? p->chunk : 64;
+    if (ckpt_every < 0 || ckpt_every % C != 0) return GDN_ERR_BAD_SHAPE;
+    if (ckpt_every == 0 && h_ckpt) return GDN_ERR_BAD_SHAPE;
+    return prefill_impl(p, q, k, v, log_g, beta, nullptr, nullptr, h0, hT, o, h_ckpt, ckpt_every,
+                        nullptr, 0, hip_stream, nullptr, -1, true);
 }
 
 }  // extern "C"

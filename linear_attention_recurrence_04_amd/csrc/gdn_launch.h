@@ -52,6 +52,10 @@ bool prefill_mfma_supported(const PrefillArgs& a);
 size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
 
+// The same bf16 MFMA path (same supported shapes) in one kernel: every
+// per-chunk intermediate stays on chip (no workspace).
+hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t stream);
+
 // hT = h0 (or zeros) without touching anything else (T == 0).
 hipError_t launch_state_copy(const float* h0, float* hT, size_t n, hipStream_t stream);
 

@@ -100,8 +100,8 @@ def test_workspace_query():
     assert B.gdn_chunk_prefill_workspace_bytes(P(Hv=3)) == 0   # invalid -> 0 as documented
 
 
-@pytest.mark.parametrize("Bn,T,Hk,Hv", [(1, 1, 1, 1), (2, 200, 1, 3), (1, 16384, 16, 48),
-                                        (3, 16400, 2, 6)])
+@pytest.mark.parametrize("Bn,T,Hk,Hv", [(1, 1, 1, 1), (2, 200, 1, 3), (1, 768, 16, 48),
+                                        (1, 769, 16, 48), (1, 16384, 16, 48), (3, 16400, 2, 6)])
 def test_mfma_workspace_bytes_as_documented(Bn, T, Hk, Hv):
     """bf16, d = 128, chunk 64 takes the MFMA path, whose workspace is 13568
     bytes per (sequence, value head, chunk of 64)."""
@@ -204,3 +204,23 @@ def test_varlen_prefill_rejects_bad_arguments():
     # o sized by total_tokens: an hT just past a 300-token o does not overlap it,
     # one starting inside it does (2 heads x 64 x 4 bytes per token)
     assert prefill_varlen(P(B=3, T=128), hT=fake(7, 300 * 2 * 64 * 4 - 16)) == 7
+
+
+def onchip(prob, every=0, ck=None, q=fake(0), k=fake(1), v=fake(2), lg=fake(3), bt=fake(4),
+           h0=None, hT=fake(6), o=fake(7)):
+    return B.lib().gdn_chunk_prefill_onchip(ctypes.byref(prob), q, k, v, lg, bt, h0, hT, o, ck,
+                                            every, None)
+
+
+def test_onchip_prefill_rejects_bad_arguments():
+    """The workspace-free prefill checks its arguments like the others: the
+    checkpoint spacing, null and misaligned pointers, overlapping outputs."""
+    assert onchip(P(), every=48) == 2                  # not a multiple of chunk 32
+    assert onchip(P(), every=-32) == 2
+    assert onchip(P(), every=0, ck=fake(8)) == 2       # slots without a spacing
+    assert onchip(P(), every=32) == 1                  # spacing without slots
+    assert onchip(P(), q=None) == 1
+    assert onchip(P(), q=fake(0, 4)) == 4
+    big = P(T=128, dk=128, dv=128, chunk=64, dtype=1)
+    assert onchip(big, o=fake(0)) == 7                 # o over q
+    assert onchip(P(chunk=48)) == 3
