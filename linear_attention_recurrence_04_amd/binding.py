@@ -79,6 +79,11 @@ def lib():
                                            vp]
     L.gdn_decode_step.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [pp, vp, vp, vp, fp, fp, fp, vp, vp]
+    # calibration kernels (include/gdn_calib.h)
+    L.gdn_calib_copy.restype = ctypes.c_int
+    L.gdn_calib_copy.argtypes = [vp, vp, sz, ctypes.c_int32, vp]
+    L.gdn_calib_mfma_loop.restype = ctypes.c_int
+    L.gdn_calib_mfma_loop.argtypes = [fp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
     _lib = L
     return L
 
@@ -517,3 +522,34 @@ def gdn_chunk_prefill_onchip(q, k, v, log_g, beta, h0=None, *, ckpt_every: int =
                                         ck_ptr, every, _stream(stream))
     _check(st)
     return out, hT, (h_ckpt if every > 0 else None)
+
+
+# ---------------------------------------------------------------------------
+# calibration kernels (include/gdn_calib.h): achieved peaks of this GPU
+# ---------------------------------------------------------------------------
+
+CALIB_MFMA_FLOPS = {0: 2 * 16 * 16 * 32, 1: 2 * 32 * 32 * 16}   # per instruction
+CALIB_MFMA_CHAINS = 8
+
+
+def gdn_calib_copy(src, dst, *, variant: int = 0, stream=None):
+    """Copy src into dst (same byte size, contiguous device tensors) with the
+    in-library streaming copy kernel."""
+    _need(src, "src")
+    _need(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    _check(lib().gdn_calib_copy(_ptr(src), _ptr(dst), nbytes, int(variant), _stream(stream)))
+
+
+def gdn_calib_mfma_loop(out, workgroups: int, iters: int, *, variant: int = 0, stream=None) -> float:
+    """Run the bf16 matrix-core loop; out holds workgroups * 4 floats.  Returns
+    the flops the launch performs."""
+    torch = _torch()
+    _need(out, "out", torch.float32)
+    if out.numel() < 4 * int(workgroups):
+        raise ValueError("out must hold 4 floats per workgroup")
+    _check(lib().gdn_calib_mfma_loop(_ptr(out), int(workgroups), int(iters), int(variant),
+                                     _stream(stream)))
+    return float(workgroups) * 4 * iters * CALIB_MFMA_CHAINS * CALIB_MFMA_FLOPS[int(variant)]

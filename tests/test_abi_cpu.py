@@ -1,6 +1,7 @@
 """The C-ABI library on the CPU: it loads, exports every declared symbol, and
 rejects bad arguments before touching the GPU (no compute calls here)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -9,19 +10,22 @@ import pytest
 from linear_attention_recurrence_04_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gdn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
+    assert {os.path.basename(h) for h in HEADERS} >= {"gdn.h", "gdn_calib.h"}
     for n in ("gdn_chunk_prefill", "gdn_decode_step", "gdn_chunk_prefill_workspace_bytes",
-              "gdn_status_string", "gdn_abi_version"):
+              "gdn_status_string", "gdn_abi_version", "gdn_calib_copy", "gdn_calib_mfma_loop"):
         assert n in names
 
 
@@ -224,3 +228,22 @@ def test_onchip_prefill_rejects_bad_arguments():
     big = P(T=128, dk=128, dv=128, chunk=64, dtype=1)
     assert onchip(big, o=fake(0)) == 7                 # o over q
     assert onchip(P(chunk=48)) == 3
+
+
+def test_calibration_kernels_reject_bad_arguments():
+    """The copy and matrix-core calibration calls check their arguments on the
+    host and enqueue nothing when they refuse (only refusals are called here)."""
+    L = B.lib()
+    a, b = 1 << 20, 1 << 21          # fake 16-byte-aligned device addresses (never launched)
+    assert L.gdn_calib_copy(a, b, 4096, 3, None) == 3          # variant
+    assert L.gdn_calib_copy(a, b, 4100, 0, None) == 2          # bytes % 16
+    assert L.gdn_calib_copy(None, b, 4096, 0, None) == 1
+    assert L.gdn_calib_copy(a, None, 4096, 0, None) == 1
+    assert L.gdn_calib_copy(a + 8, b, 4096, 0, None) == 4
+    assert L.gdn_calib_copy(a, a + 2048, 4096, 0, None) == 2   # overlapping ranges
+    assert L.gdn_calib_copy(None, None, 0, 0, None) == 0       # nothing to do
+    assert L.gdn_calib_mfma_loop(None, 4, 4, 0, None) == 1
+    assert L.gdn_calib_mfma_loop(a + 4, 4, 4, 0, None) == 4
+    assert L.gdn_calib_mfma_loop(a, 0, 4, 0, None) == 2
+    assert L.gdn_calib_mfma_loop(a, 4, 0, 0, None) == 2
+    assert L.gdn_calib_mfma_loop(a, 4, 4, 2, None) == 3
