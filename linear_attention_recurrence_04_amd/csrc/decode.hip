@@ -16,36 +16,75 @@
 // once and written once per call, and optionally also stored after every
 // token (the per-token states a verifier rolls back to).
 //
-// Mapping: one workgroup of NT threads per (b, h).  A thread owns a float4
-// column strip of D/RG rows (RG = row groups), held in VGPRs between the read
-// and the write; rows are interleaved so each wave load covers whole 512-byte
-// rows (fully coalesced 16-byte accesses).  Column reductions over the rows
-// combine per-thread partials in LDS in a fixed order (deterministic).
-// NT is 256 for several tokens per call and for head dim 64; a single step
-// at head dim 128 uses 512 threads (8 rows per thread), or 1024 (4 rows) once
-// the whole state no longer fits the 256 MB Infinity Cache and streams from
-// HBM (measured on the 27B head shape: 64 sequences, 201 MB of state, 512
-// threads -2% against 256, 1024 threads +27%; 128 sequences, 403 MB, 1024
-// threads -7%).
+// Mapping: one workgroup of NT threads per column block of CB state columns
+// of one (b, h) (CB = D: the whole head).  Columns are independent (every
+// reduction runs over rows), so a block needs no other workgroup.  A thread
+// owns a float4 column strip of D/RG rows (RG = row groups), held in VGPRs
+// between the read and the write; rows are interleaved so each wave load
+// covers whole rows of the block (coalesced 16-byte accesses).  Column sums
+// over the rows combine per-thread partials in LDS in two fixed-order stages
+// (deterministic): every thread adds 4 row groups of one column, then one
+// thread per column adds the RG/4 parts.
+//
+// A single step at head dim 128 runs 1024 threads per head (4 rows per
+// thread, 44 VGPRs: two workgroups per CU) with non-temporal state loads and
+// stores through a buffer resource on the head.  The state is streamed: in a
+// model the other layers' states pass through the caches between two steps
+// of one layer.  Measured on MI355X, B=128 and B=64 with the state cycled
+// over four buffers (both past the 256 MB Infinity Cache): 5.85 and 5.7 TB/s,
+// against 6.1 TB/s for the best plain copy kernel; 256 to 512 threads per
+// block of 32 to 128 columns, plain accesses, or a workgroup that walks
+// several blocks and prefetches the next were all slower there.  Plain
+// accesses keep a state that fits the Infinity Cache resident from step to
+// step (6.5 TB/s at B=64 on one buffer), which a model never sees.
+// Several tokens per call and head dim 64 use 256 threads and plain accesses.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 
-template <int D, typename TIn, bool MULTI, int NTHR>
-__global__ __launch_bounds__(NTHR) void decode_step_kernel(
+typedef __attribute__((ext_vector_type(4))) float f32v4;
+
+// 16-byte state access; NTS bit 0: non-temporal loads, bit 1: non-temporal
+// stores (streaming: no reuse expected)
+template <int NTS>
+__device__ __forceinline__ float4 load_state(const float* p) {
+    if constexpr ((NTS & 1) != 0) {
+        const f32v4 x = __builtin_nontemporal_load(reinterpret_cast<const f32v4*>(p));
+        return make_float4(x[0], x[1], x[2], x[3]);
+    } else {
+        return *reinterpret_cast<const float4*>(p);
+    }
+}
+
+template <int NTS>
+__device__ __forceinline__ void store_state(float* p, const float4& v) {
+    if constexpr ((NTS & 2) != 0) {
+        const f32v4 x = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(x, reinterpret_cast<f32v4*>(p));
+    } else {
+        *reinterpret_cast<float4*>(p) = v;
+    }
+}
+
+template <int D, typename TIn, bool MULTI, int NTHR, int CB, int NTS>
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 8))) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ log_g, const float* __restrict__ beta,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     float* __restrict__ state, TIn* __restrict__ o, float* __restrict__ states,
     int T, int Hk, int Hv, int l2norm, float q_scale) {
     constexpr int NT = NTHR;
-    constexpr int CG = D / 4;     // float4 column groups per row
+    constexpr int NCB = D / CB;   // column blocks per (b, h): one workgroup each
+    constexpr int CG = CB / 4;    // float4 column groups per row of the block
     constexpr int RG = NT / CG;   // row groups
     constexpr int RPT = D / RG;   // rows per thread
-    static_assert(RPT * RG == D && CG * RG == NT, "decode tiling");
+    static_assert(RPT * RG == D && CG * RG == NT && NCB * CB == D, "decode tiling");
+    static_assert(NT >= D, "one thread per element of q and k");
+    static_assert(!MULTI || NCB == 1, "several tokens per call keep the whole head");
 
-    const int bh = blockIdx.x;    // b * Hv + h
+    const int bh = blockIdx.x / NCB;   // b * Hv + h
+    const int c0 = (blockIdx.x - bh * NCB) * CB;   // first state column of the block
     const int b = bh / Hv;
     const int h = bh - b * Hv;
     const int hk = h / (Hv / Hk);
@@ -53,19 +92,50 @@ __global__ __launch_bounds__(NTHR) void decode_step_kernel(
     const int cg = tid % CG;
     const int rg = tid / CG;
 
-    __shared__ float kh[D];
-    __shared__ float qh[D];
-    __shared__ float red[2][RG][D];
-    __shared__ float wsum[NT / 64][3];
-    __shared__ float dl[D];
+    __shared__ __align__(16) float kh[D];
+    __shared__ __align__(16) float qh[D];
+    constexpr int NP = RG / 4;   // column sums in two stages: NP parts of 4 row groups
+    static_assert(NP * 4 == RG && NP * CB == NT, "two-stage column sum");
+    __shared__ __align__(16) float red[2][RG][CB];
+    __shared__ __align__(16) float red2[2][NP][CB];
+    __shared__ __align__(16) float wsum[NT / 64][3];
+    __shared__ __align__(16) float dl[CB];   // read as float4
 
-    float* S = state + (size_t)bh * D * D;
+    float* S = state + (size_t)bh * D * D + c0;
 
-    // 1. stream this head's state into registers (all loads in flight at once)
+    // A single step issues its small loads (q, k, v, the gates) before the
+    // state: memory waits complete in issue order, so the norms below can
+    // then run while the state is still in flight.  Every lane loads (the
+    // indices are clamped), so no branch splits the waits.
+    TIn k0 = TIn(), q0 = TIn(), v0 = TIn();
+    float lg0 = 0.f, bt0 = 0.f;
+    if constexpr (!MULTI) {
+        const size_t off = ((size_t)b * Hk + hk) * D + (tid < D ? tid : D - 1);
+        k0 = k[off];
+        q0 = q[off];
+        v0 = v[(size_t)bh * D + c0 + (tid < CB ? tid : CB - 1)];
+        lg0 = log_g[bh];
+        bt0 = beta[bh];
+    }
+
+    // 1. stream this block of the state into registers (all loads in flight at
+    //    once).  A single step addresses it through a buffer resource on the
+    //    block: one VGPR offset per thread, the row step in a scalar offset.
     float4 s[RPT];
+    __amdgpu_buffer_rsrc_t srs;
+    const int voff = ((rg * D) + 4 * cg) * 4;   // bytes
+    if constexpr (!MULTI) {
+        srs = __builtin_amdgcn_make_buffer_rsrc(S, (short)0, (D * D - c0) * 4, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-        s[i] = *reinterpret_cast<const float4*>(S + (size_t)(rg + RG * i) * D + 4 * cg);
+        for (int i = 0; i < RPT; ++i) {
+            const f32v4 x = __builtin_amdgcn_raw_buffer_load_b128(srs, voff, i * RG * D * 4,
+                                                                  (NTS & 1) ? 2 : 0);
+            s[i] = make_float4(x[0], x[1], x[2], x[3]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) s[i] = load_state<NTS>(S + (size_t)(rg + RG * i) * D + 4 * cg);
+    }
 
     const int NTOK = MULTI ? T : 1;   // a single step compiles to straight-line code
     for (int t = 0; t < NTOK; ++t) {
@@ -75,7 +145,10 @@ __global__ __launch_bounds__(NTHR) void decode_step_kernel(
 
         // 2. q, k of the key head, normalised in fp32
         float kv = 0.f, qv = 0.f;
-        if (tid < D) {
+        if constexpr (!MULTI) {
+            kv = tid < D ? to_f32(k0) : 0.f;
+            qv = tid < D ? to_f32(q0) : 0.f;
+        } else if (tid < D) {
             const size_t off = (bt_idx * Hk + hk) * D + tid;
             kv = to_f32(k[off]);
             qv = to_f32(q[off]);
@@ -123,29 +196,40 @@ __global__ __launch_bounds__(NTHR) void decode_step_kernel(
             red[1][rg][4 * cg + c] = pc[c];
         }
         __syncthreads();
+        {   // every thread: one column's sum over 4 row groups
+            const int col = tid % CB, part = tid / CB;
+            float a4 = 0.f, c4 = 0.f;
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                a4 += red[0][4 * part + r][col];
+                c4 += red[1][4 * part + r][col];
+            }
+            red2[0][part][col] = a4;
+            red2[1][part][col] = c4;
+        }
+        __syncthreads();
 
         // 4. column totals, delta and the output (one thread per column)
-        float lgv = log_g[row], bt = beta[row];
+        float lgv = MULTI ? log_g[row] : lg0, bt = MULTI ? beta[row] : bt0;
         if (A_log) {   // raw projections a, b
-            const int h = bh % Hv;
             lgv = raw_log_decay(lgv, A_log[h], dt_bias[h]);
             bt = raw_beta(bt);
         }
         const float g = expf(lgv);
-        if (tid < D) {
+        if (tid < CB) {
             float a = 0.f, c = 0.f;
     #pragma unroll
-            for (int r = 0; r < RG; ++r) {
-                a += red[0][r][tid];
-                c += red[1][r][tid];
+            for (int r = 0; r < NP; ++r) {
+                a += red2[0][r][tid];
+                c += red2[1][r][tid];
             }
             float kq = 0.f;
     #pragma unroll
             for (int w = 0; w < (D + 63) / 64; ++w) kq += wsum[w][2];
-            const float vj = to_f32(v[row * D + tid]);
+            const float vj = MULTI ? to_f32(v[row * D + c0 + tid]) : to_f32(v0);
             const float delta = bt * (vj - g * a);
             dl[tid] = delta;
-            o[row * D + tid] = from_f32<TIn>(q_scale * (g * c + delta * kq));
+            o[row * D + c0 + tid] = from_f32<TIn>(q_scale * (g * c + delta * kq));
         }
         __syncthreads();
 
@@ -159,10 +243,12 @@ __global__ __launch_bounds__(NTHR) void decode_step_kernel(
             n.y = g * s[i].y + kr * d4.y;
             n.z = g * s[i].z + kr * d4.z;
             n.w = g * s[i].w + kr * d4.w;
-            if (MULTI)
+            if (MULTI) {
                 s[i] = n;
-            else   // a single step writes back over the same addresses at once
-                *reinterpret_cast<float4*>(S + (size_t)(rg + RG * i) * D + 4 * cg) = n;
+            } else {   // a single step writes back over the same addresses at once
+                const f32v4 x = {n.x, n.y, n.z, n.w};
+                __builtin_amdgcn_raw_buffer_store_b128(x, srs, voff, i * RG * D * 4, (NTS & 2) ? 2 : 0);
+            }
         }
         if (MULTI && states) {
             float* St = states + row * D * D;
@@ -179,32 +265,27 @@ __global__ __launch_bounds__(NTHR) void decode_step_kernel(
     }
 }
 
-template <int D, typename TIn, int NTHR>
-static void launch_single(const DecodeArgs& a, int blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_step_kernel<D, TIn, false, NTHR>), dim3(blocks), dim3(NTHR), 0, stream,
-                       static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+template <int D, typename TIn, int NTHR, int CB, int NTS>
+static void launch_single(const DecodeArgs& a, hipStream_t stream) {
+    const int blocks = a.B * a.Hv * (D / CB);
+    hipLaunchKernelGGL((decode_step_kernel<D, TIn, false, NTHR, CB, NTS>), dim3(blocks), dim3(NTHR), 0,
+                       stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.v), a.log_g, a.beta, a.A_log, a.dt_bias,
                        a.state, static_cast<TIn*>(a.o), nullptr, 1, a.Hk, a.Hv, a.l2norm, a.q_scale);
 }
 
-// bytes of decode state beyond which a single step streams it from HBM
-constexpr size_t kInfinityCacheBytes = size_t(256) << 20;
-
 template <int D, typename TIn>
 static hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-    const int blocks = a.B * a.Hv;
-    if (blocks == 0 || a.T == 0) return hipSuccess;
+    const int heads = a.B * a.Hv;
+    if (heads == 0 || a.T == 0) return hipSuccess;
     if (a.T == 1 && !a.states) {
-        if constexpr (D == 128) {
-            const size_t state_bytes = (size_t)blocks * D * D * sizeof(float);
-            if (state_bytes > kInfinityCacheBytes) launch_single<D, TIn, 1024>(a, blocks, stream);
-            else launch_single<D, TIn, 512>(a, blocks, stream);
-        } else {
-            launch_single<D, TIn, 256>(a, blocks, stream);
-        }
+        if constexpr (D == 128)
+            launch_single<D, TIn, 1024, D, 3>(a, stream);   // non-temporal state loads and stores
+        else
+            launch_single<D, TIn, 256, D, 0>(a, stream);
     } else
-        hipLaunchKernelGGL((decode_step_kernel<D, TIn, true, 256>), dim3(blocks), dim3(256), 0, stream,
-                           static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+        hipLaunchKernelGGL((decode_step_kernel<D, TIn, true, 256, D, 0>), dim3(heads), dim3(256), 0,
+                           stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                            static_cast<const TIn*>(a.v), a.log_g, a.beta, a.A_log, a.dt_bias,
                            a.state, static_cast<TIn*>(a.o), a.states, a.T, a.Hk, a.Hv, a.l2norm,
                            a.q_scale);
