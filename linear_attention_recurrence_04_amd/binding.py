@@ -48,6 +48,11 @@ def lib():
     if not os.path.exists(LIBRARY):
         raise RuntimeError(f"{LIBRARY} is missing: build it with "
                            "`python -m linear_attention_recurrence_04_amd.build`")
+    # torch first: its HIP runtime (which it loads under the name
+    # libamdhip64.so) must be the one libgdn.so binds to (libamdhip64.so.7).
+    # Loaded the other way round, the process ends up with two HIP runtimes
+    # and the library's own one sees no device and none of torch's streams.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIBRARY)
     vp, fp, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
     pp = ctypes.POINTER(GdnProblem)

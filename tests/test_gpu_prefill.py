@@ -1,4 +1,6 @@
 """GPU parity of gdn_chunk_prefill against the fp64 oracle (small and ragged cases)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -329,3 +331,34 @@ def test_stream_argument_owns_its_allocations():
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(hT, h_ref), rep
         del junk
+
+
+def test_library_loaded_before_torch_shares_its_runtime():
+    """Loading the library before torch is imported must still leave one HIP
+    runtime in the process: a fresh interpreter queries the library first,
+    then runs a prefill through torch tensors and checks it against the
+    oracle-free invariant hT(T=0) = h0 and a finite output."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from linear_attention_recurrence_04_amd import binding as gdn\n"
+        "assert gdn.gdn_abi_version() == 1\n"
+        "import torch\n"
+        "q = torch.randn(1, 130, 1, 128, device='cuda').to(torch.bfloat16)\n"
+        "v = torch.randn(1, 130, 3, 128, device='cuda').to(torch.bfloat16)\n"
+        "lg = -torch.rand(1, 130, 3, device='cuda') * 0.1\n"
+        "bt = torch.rand(1, 130, 3, device='cuda')\n"
+        "h0 = torch.randn(1, 3, 128, 128, device='cuda') * 0.02\n"
+        "o, hT = gdn.gdn_chunk_prefill(q, q.clone(), v, lg, bt, h0)\n"
+        "torch.cuda.synchronize()\n"
+        "assert torch.isfinite(o.float()).all() and torch.isfinite(hT).all()\n"
+        "o0, h00 = gdn.gdn_chunk_prefill(q[:, :0].contiguous(), q[:, :0].contiguous(),\n"
+        "                                v[:, :0].contiguous(), lg[:, :0].contiguous(),\n"
+        "                                bt[:, :0].contiguous(), h0)\n"
+        "torch.cuda.synchronize()\n"
+        "assert torch.equal(h00, h0)\n"
+        "print('ok')\n" % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=100)
+    say(r.stdout[-500:] + r.stderr[-1500:])
+    assert r.returncode == 0 and "ok" in r.stdout
