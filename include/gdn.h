@@ -22,7 +22,9 @@
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
  *    library allocates no memory, creates no stream or event and keeps no
  *    global state: a call enqueues kernels on the caller's stream only, so
- *    calls on different streams never wait on one another.
+ *    calls on different streams never wait on one another.  The one
+ *    exception is gdn_chunk_prefill_noalloc, whose workspace is a fixed
+ *    device array of the library (see there).
  *  - Tensors are dense, row-major, innermost dimension last, exactly as listed;
  *    no strides.  Every pointer must be 16-byte aligned.
  *  - q, k, v and o share one storage dtype (gdn_problem.dtype).  log_g, beta
@@ -243,6 +245,38 @@ gdn_status gdn_chunk_prefill_onchip(const gdn_problem* problem,
                                     const float* h0, float* hT, void* o,
                                     float* h_ckpt, int32_t ckpt_every,
                                     void* hip_stream);
+
+/*
+ * gdn_chunk_prefill for callers that cannot allocate device memory: code
+ * recorded under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Arguments, checks, kernels and results are those of
+ * gdn_chunk_prefill (bitwise the same outputs), except that the workspace is
+ * a fixed array of gdn_chunk_prefill_noalloc_max_workspace() bytes (64 MiB)
+ * that the library holds on every GPU it runs on, from module load until the
+ * process ends; the call itself allocates nothing.
+ *
+ *  - A problem whose gdn_chunk_prefill_workspace_bytes() exceeds that size
+ *    is rejected with GDN_ERR_WORKSPACE before anything is enqueued (at the
+ *    27B head shape, 48 value heads, 64 MiB covers B * T up to 6592 tokens;
+ *    a longer sequence can be processed as consecutive calls carrying the
+ *    state, split at multiples of the chunk: bitwise the same results).
+ *  - Every call on one GPU uses the same array and leaves its contents
+ *    behind.  Calls whose kernels may overlap in time on one GPU (different
+ *    streams with no ordering between them) race on it and give wrong
+ *    results: order them (one stream, or events).
+ *  - The stream must belong to the current device (GDN_ERR_UNSUPPORTED
+ *    otherwise).  The first call on a device looks up the array's address
+ *    (hipGetSymbolAddress; GDN_ERR_HIP if that fails): make it outside graph
+ *    capture, then capture freely.
+ */
+gdn_status gdn_chunk_prefill_noalloc(const gdn_problem* problem,
+                                     const void* q, const void* k, const void* v,
+                                     const float* log_g, const float* beta,
+                                     const float* h0, float* hT, void* o,
+                                     void* hip_stream);
+
+/* Size in bytes of gdn_chunk_prefill_noalloc's fixed workspace array. */
+size_t gdn_chunk_prefill_noalloc_max_workspace(void);
 
 /*
  * Multi-token decode: problem->T >= 0 tokens per sequence applied in order to

@@ -84,6 +84,10 @@ def lib():
                                            vp]
     L.gdn_decode_step.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [pp, vp, vp, vp, fp, fp, fp, vp, vp]
+    L.gdn_chunk_prefill_noalloc.restype = ctypes.c_int
+    L.gdn_chunk_prefill_noalloc.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, vp, vp]
+    L.gdn_chunk_prefill_noalloc_max_workspace.restype = sz
+    L.gdn_chunk_prefill_noalloc_max_workspace.argtypes = []
     # calibration kernels (include/gdn_calib.h)
     L.gdn_calib_copy.restype = ctypes.c_int
     L.gdn_calib_copy.argtypes = [vp, vp, sz, ctypes.c_int32, vp]
@@ -527,6 +531,45 @@ def gdn_chunk_prefill_onchip(q, k, v, log_g, beta, h0=None, *, ckpt_every: int =
                                         ck_ptr, every, _stream(stream))
     _check(st)
     return out, hT, (h_ckpt if every > 0 else None)
+
+
+def gdn_chunk_prefill_noalloc_max_workspace() -> int:
+    return int(lib().gdn_chunk_prefill_noalloc_max_workspace())
+
+
+@_on_stream
+def gdn_chunk_prefill_noalloc(q, k, v, log_g, beta, h0=None, *, chunk: int = 64,
+                              qk_l2norm: bool = True, q_scale: float = 1.0, out=None, hT=None,
+                              want_state: bool = True, stream=None):
+    """gdn_chunk_prefill with the library's fixed per-device workspace array
+    (the C call allocates nothing; pass ``out`` and ``hT`` to allocate nothing
+    here either).  Returns (o, hT or None)."""
+    torch = _torch()
+    _need(q, "q")
+    dt = _dtype_code(q)
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    _need(k, "k", q.dtype, q.shape)
+    _need(v, "v", q.dtype, (B, T, Hv, dv))
+    _need(log_g, "log_g", torch.float32, (B, T, Hv))
+    _need(beta, "beta", torch.float32, (B, T, Hv))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, Hv, dk, dv))
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(out, "out", q.dtype, (B, T, Hv, dv))
+    if hT is None and want_state:
+        hT = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=q.device)
+    elif hT is not None:
+        _need(hT, "hT", torch.float32, (B, Hv, dk, dv))
+    prob = make_problem(B, T, Hk, Hv, dk, dv, chunk=chunk, dtype=dt, qk_l2norm=qk_l2norm,
+                        q_scale=q_scale)
+    st = lib().gdn_chunk_prefill_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(log_g), _ptr(beta), _ptr(h0), _ptr(hT), _ptr(out),
+                                         _stream(stream))
+    _check(st)
+    return out, hT
 
 
 # ---------------------------------------------------------------------------

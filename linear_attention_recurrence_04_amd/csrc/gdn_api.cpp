@@ -189,6 +189,16 @@ gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, cons
 
 }  // namespace
 
+int gdn::prefill_checked(const void* problem, const void* q, const void* k, const void* v,
+                         const float* log_g, const float* beta, const float* h0, float* hT,
+                         void* o, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const gdn_problem* p = static_cast<const gdn_problem*>(problem);
+    const gdn_status st = check_problem(p, false);
+    if (st != GDN_OK) return st;
+    return prefill_impl(p, q, k, v, log_g, beta, nullptr, nullptr, h0, hT, o, nullptr, 0,
+                        workspace, workspace_bytes, hip_stream);
+}
+
 extern "C" {
 
 gdn_status gdn_chunk_prefill(const gdn_problem* p, const void* q, const void* k, const void* v,

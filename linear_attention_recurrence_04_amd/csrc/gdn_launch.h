@@ -59,4 +59,10 @@ hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t stream);
 // hT = h0 (or zeros) without touching anything else (T == 0).
 hipError_t launch_state_copy(const float* h0, float* hT, size_t n, hipStream_t stream);
 
+// gdn_chunk_prefill's checks and dispatch with the workspace given by the
+// caller of this function (gdn_api.cpp); returns a gdn_status value.
+int prefill_checked(const void* problem, const void* q, const void* k, const void* v,
+                    const float* log_g, const float* beta, const float* h0, float* hT, void* o,
+                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
 }  // namespace gdn

@@ -247,3 +247,20 @@ def test_calibration_kernels_reject_bad_arguments():
     assert L.gdn_calib_mfma_loop(a, 0, 4, 0, None) == 2
     assert L.gdn_calib_mfma_loop(a, 4, 0, 0, None) == 2
     assert L.gdn_calib_mfma_loop(a, 4, 4, 2, None) == 3
+
+
+def test_noalloc_prefill_refuses_before_any_device_call():
+    """gdn_chunk_prefill_noalloc checks the problem and the size of its fixed
+    array on the host: a NULL problem, a bad problem and a problem whose
+    workspace exceeds the 64 MiB array are refused without touching a GPU."""
+    L = B.lib()
+    assert L.gdn_chunk_prefill_noalloc_max_workspace() == 64 << 20
+    fake = 1 << 20
+    args = [fake, fake, fake, fake, fake, None, fake, fake, None]
+    assert L.gdn_chunk_prefill_noalloc(None, *args) == 1
+    big = B.make_problem(1, 6593, 16, 48, 128, 128)        # 104 chunks x 48 heads x 13568 B
+    assert L.gdn_chunk_prefill_noalloc(ctypes.byref(big), *args) == 5
+    big2 = B.make_problem(2, 3400, 16, 48, 128, 128)
+    assert L.gdn_chunk_prefill_noalloc(ctypes.byref(big2), *args) == 5
+    bad = B.make_problem(1, 64, 16, 40, 128, 128)          # Hv % Hk != 0
+    assert L.gdn_chunk_prefill_noalloc(ctypes.byref(bad), *args) == 2
