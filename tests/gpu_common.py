@@ -99,3 +99,12 @@ def assert_parity(o_gpu, o_ref, h_gpu, h_ref, dtype: str, label: str = ""):
             assert per_head_rel(o_gpu, o_ref, (0, 2)) <= BF16_REL, label
         assert per_head_rel(h_gpu, h_ref, (0, 1)) <= BF16_REL, label
     return mo, mh
+
+
+def margins(o_gpu, o_ref, h_gpu, h_ref, label: str, o_heads=(0, 2), h_heads=(0, 1)) -> dict:
+    """Print and return the worst relative error of any (sequence, head) slab
+    of o and of the state, beside the bar."""
+    wo = per_head_rel(o_gpu, o_ref, o_heads) if o_gpu is not None and o_gpu.size else 0.0
+    wh = per_head_rel(h_gpu, h_ref, h_heads) if h_gpu is not None else 0.0
+    say(f"  margins {label}: worst per-(b,h) rel o {wo:.3e}, hT {wh:.3e} (bar {BF16_REL:.0e})")
+    return {"o": wo, "hT": wh}

@@ -128,3 +128,41 @@ def test_decode_empty_batch():
                             torch.zeros((0, 1), device="cuda"),
                             torch.zeros((0, 1, 64, 64), device="cuda"))
     assert o.shape == (0, 1, 64)
+
+
+@pytest.mark.parametrize("field", ["log_g", "v", "beta", "state"])
+def test_decode_nan_stays_in_its_head(field):
+    """27B head shape, 8 sequences, 3 steps: a NaN in one (sequence, value
+    head)'s gate, v, beta or state leaves every other (sequence, head) state
+    and output bitwise as in the clean run."""
+    torch = torch_mod()
+    p = gi.DecodeProblem("t", 8, 16, 48, 128, 128, 3, "bf16")
+    st = gi.make_decode_steps(p, 7)
+    s0 = gi.make_decode_state(p, 7)
+    b, h = 3, 40
+
+    def run(poison):
+        state = dev32(s0)
+        if poison and field == "state":
+            state[b, h, 5, 9] = float("nan")
+        outs = []
+        for s in range(p.steps):
+            x = {n: st[n][s].copy() for n in st}
+            if poison and s == 1 and field != "state":
+                if field == "v":
+                    x["v"][b, h, 3] = np.nan
+                else:
+                    x[field][b, h] = np.nan
+            outs.append(gdn.gdn_decode_step(dev(x["q"], "bf16"), dev(x["k"], "bf16"),
+                                            dev(x["v"], "bf16"), dev32(x["log_g"]),
+                                            dev32(x["beta"]), state))
+        torch.cuda.synchronize()
+        return torch.stack(outs), state
+
+    o_c, s_c = run(False)
+    o_n, s_n = run(True)
+    mask = torch.ones((p.B, p.Hv), dtype=torch.bool, device="cuda")
+    mask[b, h] = False
+    assert torch.equal(o_n[:, mask], o_c[:, mask])
+    assert torch.equal(s_n[mask], s_c[mask])
+    assert not torch.isfinite(s_n[b, h]).all()

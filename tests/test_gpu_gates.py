@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_common import (NTHREADS, assert_parity, dev, dev32, host, run_oracle, say, torch_mod)
+from gpu_common import (margins, NTHREADS, assert_parity, dev, dev32, host, run_oracle, say, torch_mod)
 from linear_attention_recurrence_04_amd import binding as gdn
 from linear_attention_recurrence_04_amd import inputs as gi
 
@@ -98,8 +98,8 @@ def test_gated_decode_matches_oracle(dtype, d):
 
 
 def test_qwen27b_gated_full_size():
-    """27B prefill workload with raw gates (MFMA path): group 11 against the
-    oracle; one 27B decode step (B=64) with raw gates on every head."""
+    """27B prefill workload with raw gates (MFMA path): all 48 heads against
+    the oracle; one 27B decode step (B=64) with raw gates on every head."""
     torch = torch_mod()
     p = gi.QWEN27B_PREFILL
     say(f"{p.name}: gated")
@@ -107,15 +107,12 @@ def test_qwen27b_gated_full_size():
     rg = gi.make_raw_gates((p.B, p.T), p.Hv, seed=0)
     o, hT, _ = run_gated(inp, rg, "bf16", p.chunk)
     o, hT = host(o), host(hT)
-    r = p.Hv // p.Hk
-    hk = 11
-    hs = slice(hk * r, (hk + 1) * r)
-    lg, bt = oracle.qwen_gates(rg["a"][:, :, hs], rg["b"][:, :, hs], rg["A_log"][hs],
-                               rg["dt_bias"][hs])
-    say(f"  oracle key head {hk}")
-    o_ref, h_ref = oracle.gdn_sequential(inp["q"][:, :, hk:hk + 1], inp["k"][:, :, hk:hk + 1],
-                                         inp["v"][:, :, hs], lg, bt, inp["h0"][:, hs], nthreads=r)
-    assert_parity(o[:, :, hs], o_ref, hT[:, hs], h_ref, "bf16", f"{p.name} gated group {hk}")
+    lg, bt = oracle.qwen_gates(rg["a"], rg["b"], rg["A_log"], rg["dt_bias"])
+    say("  oracle, all 48 heads")
+    o_ref, h_ref = oracle.gdn_sequential(inp["q"], inp["k"], inp["v"], lg, bt, inp["h0"],
+                                         nthreads=NTHREADS)
+    assert_parity(o, o_ref, hT, h_ref, "bf16", f"{p.name} gated")
+    margins(o, o_ref, hT, h_ref, f"{p.name} gated")
 
     d = gi.QWEN27B_DECODE
     say(f"{d.name}: one gated step, every head")

@@ -189,6 +189,30 @@ def test_nan_stays_in_its_head():
     assert not np.all(np.isfinite(hT[:, 1]))
 
 
+@pytest.mark.parametrize("field,t,h", [("log_g", 300, 4), ("v", 130, 1), ("beta", 500, 3)])
+def test_nan_stays_in_its_head_mfma(field, t, h):
+    """bf16 MFMA prefill (d=128, chunk 64, 2 key heads x 3 value heads, 700
+    tokens): a NaN in one value head's log g, v or beta at token t leaves
+    every other value head bitwise as in the clean run (also the other value
+    heads of its key head), and that head's output before t's chunk too."""
+    torch = torch_mod()
+    inp = gi.custom_prefill(1, 700, 2, 6, 128, 128, seed=21, dtype="bf16", gate="qwen", h0="normal")
+    o_c, h_c = run_prefill(inp, "bf16", 64)
+    if field == "v":
+        inp["v"][0, t, h, 17] = np.nan
+    else:
+        inp[field][0, t, h] = np.nan
+    o_n, h_n = run_prefill(inp, "bf16", 64)
+    torch.cuda.synchronize()
+    others = [x for x in range(6) if x != h]
+    assert torch.equal(o_n[:, :, others], o_c[:, :, others])
+    assert torch.equal(h_n[:, others], h_c[:, others])
+    c0 = (t // 64) * 64
+    assert torch.equal(o_n[:, :c0, h], o_c[:, :c0, h])
+    assert not torch.isfinite(h_n[:, h]).all()
+    say(f"  NaN in {field}[t={t}, h={h}]: other heads bitwise clean, head {h} clean before token {c0}")
+
+
 def test_binding_rejects_bad_layouts():
     torch = torch_mod()
     inp = gi.custom_prefill(1, 16, 1, 1, 64, 64, seed=0, dtype="f32")
