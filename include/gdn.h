@@ -67,7 +67,11 @@ typedef enum {
     GDN_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned */
     GDN_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required */
     GDN_ERR_HIP = 6,          /* the HIP runtime refused the launch */
-    GDN_ERR_ALIAS = 7         /* an output overlaps an input it may not alias */
+    GDN_ERR_ALIAS = 7,        /* an output overlaps an input it may not alias */
+    /* never returned: they make every int32 value a valid gdn_status, so a
+     * code from a newer or foreign caller can be passed to gdn_status_string */
+    GDN_STATUS_RESERVED_MIN_ = -2147483647 - 1,
+    GDN_STATUS_RESERVED_MAX_ = 2147483647
 } gdn_status;
 
 /* Per-call sizes and options. */

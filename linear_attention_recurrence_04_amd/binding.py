@@ -53,7 +53,12 @@ def lib():
     # Loaded the other way round, the process ends up with two HIP runtimes
     # and the library's own one sees no device and none of torch's streams.
     import torch  # noqa: F401
-    L = ctypes.CDLL(LIBRARY)
+    _lib = _declare(ctypes.CDLL(LIBRARY))
+    return _lib
+
+
+def _declare(L):
+    """Argument and result types of every exported call (include/*.h)."""
     vp, fp, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
     pp = ctypes.POINTER(GdnProblem)
     L.gdn_abi_version.restype = ctypes.c_int
@@ -93,7 +98,6 @@ def lib():
     L.gdn_calib_copy.argtypes = [vp, vp, sz, ctypes.c_int32, vp]
     L.gdn_calib_mfma_loop.restype = ctypes.c_int
     L.gdn_calib_mfma_loop.argtypes = [fp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
-    _lib = L
     return L
 
 

@@ -94,6 +94,7 @@ const char* gdn_status_string(gdn_status s) {
         case GDN_ERR_WORKSPACE: return "workspace missing or too small";
         case GDN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
         case GDN_ERR_ALIAS: return "an output buffer overlaps an input";
+        default: break;
     }
     return "unknown gdn_status";
 }
