@@ -133,6 +133,19 @@ def spin_up(torch, seconds: float = SPIN_UP_S):
         torch.cuda.synchronize()
 
 
+def time_loop(torch, fn, steps: int) -> float:
+    """ms for `steps` back-to-back calls between one pair of events."""
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
 def time_calls(torch, fn, steps: int) -> dict:
     """Each of `steps` back-to-back calls between its own pair of events on the
     stream the kernels run on (no host synchronisation between calls).  Returns
@@ -562,10 +575,16 @@ def bench_decode(torch, gdn, d, steps, warmup, rotate: int = 1, clock=None):
         x.copy_(state0)
     idx[0] = 0
     log(f"decode: timing {steps} steps" + (f" over {rotate} state buffers" if rotate > 1 else ""))
+    # the step loop end to end between one pair of events (the per-step mean),
+    # then again with an event pair around every step (median and spread)
     if clock is not None:
         with clock:
-            return time_calls(torch, call, steps)
-    return time_calls(torch, call, steps)
+            loop_ms = time_loop(torch, call, steps)
+    else:
+        loop_ms = time_loop(torch, call, steps)
+    t = time_calls(torch, call, steps)
+    t["loop_mean_ms"] = loop_ms / steps
+    return t
 
 
 def bench_decode_multi(torch, gdn, d, steps, warmup, tokens_per_call: int):
@@ -689,7 +708,8 @@ def main():
                     help="time only the plain prefill and decode calls (profiling runs, where "
                          "the checkpoint, raw-gate and multi-token legs would mix into the "
                          "same kernels' statistics)")
-    ap.add_argument("--only", choices=["all", "prefill", "onchip", "decode", "decode_B128", "copy"],
+    ap.add_argument("--only", choices=["all", "prefill", "onchip", "decode", "decode_rot", "decode_B128",
+                                       "copy"],
                     default="all",
                     help="restrict to one leg (profiling runs); 'copy' runs only the plain "
                          "copy kernel used to calibrate HBM byte counters")
@@ -832,6 +852,15 @@ def main():
         }
         log(f"long context: {ms_l:.3f} ms per prompt, {ms_l * 1e3 / ncalls:.1f} us per call")
 
+    if args.only == "decode_rot":
+        # profiling: the past-cache decode leg alone (4 state buffers cycled)
+        t_r = bench_decode(torch, gdn, d, args.decode_steps, min(args.warmup, 10) or 1, rotate=4)
+        ms_r = t_r["loop_mean_ms"]
+        result["value"] = round(d.B / (ms_r * 1e-3), 1)
+        result["unit"] = "tokens/s (decode)"
+        result["ms_per_step"] = round(ms_r, 5)
+        result["decode"] = {"workload": d.name, "state_buffers_cycled": 4, "timing": timing_summary(t_r),
+                            "state_update_GBps": round(decode_bytes(d) / (ms_r * 1e-3) / 1e9, 2)}
     if args.only in ("all", "decode"):
         nb = decode_bytes(d)
         src_d = source_hash("decode.hip", "gdn_device.h")
@@ -840,16 +869,17 @@ def main():
         rot = 4
         clock_d = ClockSampler(torch)
         t_r = bench_decode(torch, gdn, d, args.decode_steps, warm, rotate=rot, clock=clock_d)
-        ms_r = t_r["median_ms"]
+        ms_r = t_r["loop_mean_ms"]   # the step loop timed end to end, per-step mean
         gbps_r = nb / (ms_r * 1e-3) / 1e9
         # the same steps on one state buffer: 201 MB re-read every step stays
         # in the 256 MB Infinity Cache
         t_d = bench_decode(torch, gdn, d, args.decode_steps, warm)
-        ms_d = t_d["median_ms"]
+        ms_d = t_d["loop_mean_ms"]
         gbps_d = nb / (ms_d * 1e-3) / 1e9
         result["decode"] = {
             "workload": d.name, "steps": args.decode_steps,
             "us_per_step": round(ms_r * 1e3, 3),
+            "us_per_step_is": "mean over the step loop timed end to end (one event pair)",
             "tokens_per_s": round(d.B / (ms_r * 1e-3), 1),
             "state_update_GBps": round(gbps_r, 2),
             "state_buffers_cycled": rot, "timing": timing_summary(t_r),
@@ -874,7 +904,7 @@ def main():
         # twice the batch: 402.7 MB of state, more than the 256 MB Infinity Cache
         d2 = gi.DecodeProblem(d.name.replace("B64", "B128"), 2 * d.B, d.Hk, d.Hv, d.dk, d.dv, 200)
         t_2 = bench_decode(torch, gdn, d2, d2.steps, min(args.warmup, 10) or 1)
-        ms_2 = t_2["median_ms"]
+        ms_2 = t_2["loop_mean_ms"]
         nb2 = decode_bytes(d2)
         src_d = source_hash("decode.hip", "gdn_device.h")
         result["decode_B128"] = {"workload": d2.name, "steps": d2.steps,
