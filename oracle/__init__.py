@@ -58,6 +58,10 @@ def _declare(lib):
     lib.oracle_neumann_inverse.argtypes = [i, dp, dp]
     lib.oracle_qwen_gates.restype = i
     lib.oracle_qwen_gates.argtypes = [ctypes.c_long, i, dp, dp, dp, dp, dp, dp]
+    lib.oracle_causal_conv1d.restype = i
+    lib.oracle_causal_conv1d.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, i]
+    lib.oracle_gated_rmsnorm.restype = i
+    lib.oracle_gated_rmsnorm.argtypes = [ctypes.c_long, i, dp, dp, dp, ctypes.c_double, dp]
     return lib
 
 
@@ -173,3 +177,49 @@ def qwen_gates(a, b, A_log, dt_bias, lib=None) -> Tuple[np.ndarray, np.ndarray]:
     if rc != 0:
         raise ValueError(f"oracle_qwen_gates failed ({rc})")
     return log_g, beta
+
+
+def causal_conv1d(x, w, bias=None, state_in=None, *, silu: bool = True,
+                  lib=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Causal depthwise conv1d over the channel axis (the operations around
+    the recurrence, "Qwen3.5 Gated Delta Net NKI Kernel for AWS Neuron",
+    section "How It Works"; the carried convolution state of "Add Qwen3.6-27B
+    hybrid DeltaNet/GQA contrib model and vLLM serving path", "Summary").
+    x [B, T, C], w [C, K], bias [C] or None, state_in [B, K-1, C] or None
+    (zeros).  Returns (y [B, T, C], state_out [B, K-1, C]) in fp64."""
+    lib = lib or load()
+    x, w = _f64(x), _f64(w)
+    if x.ndim != 3 or w.ndim != 2 or w.shape[0] != x.shape[2]:
+        raise ValueError("x must be [B, T, C] and w [C, K]")
+    B, T, C = x.shape
+    K = w.shape[1]
+    bias_a = None if bias is None else _f64(bias)
+    st = None if state_in is None else _f64(state_in)
+    if st is not None and st.shape != (B, K - 1, C):
+        raise ValueError("state_in must be [B, K-1, C]")
+    y = np.zeros((B, T, C))
+    st_out = np.zeros((B, K - 1, C))
+    rc = lib.oracle_causal_conv1d(B, T, C, K, _ptr(x), _ptr(w), _ptr(bias_a), _ptr(st),
+                                  _ptr(st_out), _ptr(y), int(bool(silu)))
+    if rc != 0:
+        raise ValueError(f"oracle_causal_conv1d failed ({rc})")
+    return y, st_out
+
+
+def gated_rmsnorm(x, z, w, eps: float = 1e-6, lib=None) -> np.ndarray:
+    """y = x / sqrt(mean(x^2) + eps) * w * silu(z) over the last axis (the RMS
+    norm and gating around the recurrence, same section); z None: no gate."""
+    lib = lib or load()
+    x, w = _f64(x), _f64(w)
+    D = x.shape[-1]
+    if w.shape != (D,):
+        raise ValueError("w must hold one value per element of the last axis")
+    za = None if z is None else _f64(z)
+    if za is not None and za.shape != x.shape:
+        raise ValueError("z must have the shape of x")
+    rows = x.size // D if D else 0
+    y = np.zeros(x.shape)
+    rc = lib.oracle_gated_rmsnorm(rows, D, _ptr(x), _ptr(za), _ptr(w), float(eps), _ptr(y))
+    if rc != 0:
+        raise ValueError(f"oracle_gated_rmsnorm failed ({rc})")
+    return y

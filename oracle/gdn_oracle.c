@@ -353,3 +353,57 @@ int oracle_gdn_chunked(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
     free(S); free(Qh); free(Kh); free(gam); free(A); free(R); free(S_next);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Causal conv1d and gated RMS norm (the operations around the recurrence)  */
+/* ------------------------------------------------------------------------ */
+
+static double silu(double x) { return x / (1.0 + exp(-x)); }
+
+int oracle_causal_conv1d(int B, int T, int C, int K, const double* x, const double* w,
+                         const double* bias, const double* state_in, double* state_out,
+                         double* y, int silu_on) {
+    if (B < 0 || T < 0 || C <= 0 || K < 1) return -1;
+    if ((long)B * T > 0 && (!x || !y)) return -1;
+    if (!w) return -1;
+    const int P = K - 1;                 /* inputs carried between calls */
+    /* the whole input of one sequence with its carried prefix: u[s + P], s = -P .. T-1 */
+    double* u = (double*)malloc(sizeof(double) * (size_t)(T + P) * (size_t)C);
+    if (!u) return -2;
+    for (int b = 0; b < B; ++b) {
+        for (int i = 0; i < P; ++i)
+            for (int c = 0; c < C; ++c)
+                u[(size_t)i * C + c] = state_in ? state_in[((size_t)b * P + i) * C + c] : 0.0;
+        for (int t = 0; t < T; ++t)
+            for (int c = 0; c < C; ++c)
+                u[(size_t)(t + P) * C + c] = x[((size_t)b * T + t) * C + c];
+        for (int t = 0; t < T; ++t)
+            for (int c = 0; c < C; ++c) {
+                double acc = bias ? bias[c] : 0.0;
+                for (int j = 0; j < K; ++j) acc += w[(size_t)c * K + j] * u[(size_t)(t + j) * C + c];
+                y[((size_t)b * T + t) * C + c] = silu_on ? silu(acc) : acc;
+            }
+        if (state_out)
+            for (int i = 0; i < P; ++i)
+                for (int c = 0; c < C; ++c)
+                    state_out[((size_t)b * P + i) * C + c] = u[(size_t)(T + i) * C + c];
+    }
+    free(u);
+    return 0;
+}
+
+int oracle_gated_rmsnorm(long rows, int D, const double* x, const double* z, const double* w,
+                         double eps, double* y) {
+    if (rows < 0 || D <= 0 || eps < 0.0) return -1;
+    if (rows > 0 && (!x || !w || !y)) return -1;
+    for (long r = 0; r < rows; ++r) {
+        double ss = 0.0;
+        for (int i = 0; i < D; ++i) ss += x[r * D + i] * x[r * D + i];
+        const double inv = 1.0 / sqrt(ss / D + eps);
+        for (int i = 0; i < D; ++i) {
+            const double g = z ? silu(z[r * D + i]) : 1.0;
+            y[r * D + i] = x[r * D + i] * inv * w[i] * g;
+        }
+    }
+    return 0;
+}

@@ -75,6 +75,31 @@ int oracle_qwen_gates(long n, int Hv, const double* a, const double* b,
                       const double* A_log, const double* dt_bias,
                       double* log_g, double* beta);
 
+/* The operations around the recurrence ("Qwen3.5 Gated Delta Net NKI Kernel
+ * for AWS Neuron", section "How It Works": projections, causal conv1d,
+ * gating, RMS norm run outside the recurrence kernel; "Add Qwen3.6-27B
+ * hybrid DeltaNet/GQA contrib model and vLLM serving path", section
+ * "Summary": GDN convolution state checkpoints).  The pages give no
+ * formula; these are the plain readings:
+ *
+ * Causal depthwise conv1d over the channel axis, width K, optional bias,
+ * optional SiLU (x / (1 + e^-x)):
+ *   y[b,t,c] = act(bias[c] + sum_{j=0}^{K-1} w[c,j] * u[b, t-(K-1)+j, c])
+ * where u[b, s, c] = x[b, s, c] for s >= 0 and state_in[b, K-1+s, c] for
+ * s < 0 (zeros when state_in is NULL).  The carried state is the last K-1
+ * inputs: state_out[b, i, c] = u[b, T-(K-1)+i, c], i = 0 .. K-2 (it may be
+ * state_in itself).  Layouts: x, y [B, T, C]; w [C, K]; bias [C] or NULL;
+ * states [B, K-1, C]. */
+int oracle_causal_conv1d(int B, int T, int C, int K, const double* x, const double* w,
+                         const double* bias, const double* state_in, double* state_out,
+                         double* y, int silu);
+
+/* Gated RMS norm over the last axis of `rows` rows of D values:
+ *   y[r, i] = x[r, i] / sqrt(mean_i(x[r, i]^2) + eps) * w[i] * silu(z[r, i])
+ * (z NULL: no gate).  y may be x itself. */
+int oracle_gated_rmsnorm(long rows, int D, const double* x, const double* z, const double* w,
+                         double eps, double* y);
+
 #ifdef __cplusplus
 }
 #endif

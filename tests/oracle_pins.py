@@ -373,6 +373,121 @@ def pin_qwen_gates(lib):
     assert np.allclose(lg, -np.exp(A_log)[None, :] * np.logaddexp(0.0, x), rtol=1e-14, atol=0)
 
 
+def _silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def pin_conv_closed_forms(lib):
+    """Causal conv1d: the identity and pure-delay kernels reproduce the input
+    exactly (the delay reads the carried state for the first K-1 tokens);
+    a constant input through a full state gives act(bias + c sum w); the
+    carried state is the last K-1 inputs, mixing old state and input when
+    T < K-1; SiLU at 0, +-1 and 30 against x / (1 + e^-x)."""
+    rng = _rng(41)
+    for K in (2, 3, 4):
+        B, T, C = 2, 9, 5
+        x = rng.standard_normal((B, T, C))
+        st = rng.standard_normal((B, K - 1, C))
+        w = np.zeros((C, K))
+        w[:, K - 1] = 1.0
+        y, so = oracle.causal_conv1d(x, w, None, st, silu=False, lib=lib)
+        assert np.array_equal(y, x) and np.array_equal(so, x[:, T - (K - 1):]), K
+        w = np.zeros((C, K))
+        w[:, 0] = 1.0
+        y, _ = oracle.causal_conv1d(x, w, None, st, silu=False, lib=lib)
+        assert np.array_equal(y[:, :K - 1], st) and np.array_equal(y[:, K - 1:], x[:, :T - (K - 1)]), K
+        c = 0.37
+        w = rng.standard_normal((C, K))
+        bias = rng.standard_normal(C)
+        y, _ = oracle.causal_conv1d(np.full((B, T, C), c), w, bias, np.full((B, K - 1, C), c),
+                                    silu=True, lib=lib)
+        z = bias + c * w.sum(axis=1)
+        assert np.allclose(y, (z / (1.0 + np.exp(-z)))[None, None, :], rtol=1e-14, atol=1e-15), K
+        if K > 2:   # fewer tokens than the carried state
+            xs = x[:, :1]
+            _, so = oracle.causal_conv1d(xs, w, None, st, silu=False, lib=lib)
+            assert np.array_equal(so, np.concatenate([st, xs], axis=1)[:, 1:]), K
+    x = np.array([[[0.0], [1.0], [-1.0], [30.0]]])
+    w = np.array([[0.0, 0.0, 0.0, 1.0]])
+    y, _ = oracle.causal_conv1d(x, w, None, None, silu=True, lib=lib)
+    assert np.allclose(y[0, :, 0], [0.0, 1.0 / (1.0 + np.exp(-1.0)), -1.0 / (1.0 + np.e),
+                                    30.0 / (1.0 + np.exp(-30.0))], rtol=1e-15, atol=0)
+
+
+def pin_conv_library_correlation(lib):
+    """Every channel against numpy's correlate (an independent routine) over
+    the input with its carried prefix, plus the bias."""
+    rng = _rng(42)
+    B, T, C, K = 2, 23, 4, 4
+    x = rng.standard_normal((B, T, C))
+    st = rng.standard_normal((B, K - 1, C))
+    w = rng.standard_normal((C, K))
+    bias = rng.standard_normal(C)
+    y, _ = oracle.causal_conv1d(x, w, bias, st, silu=False, lib=lib)
+    for b in range(B):
+        for c in range(C):
+            u = np.concatenate([st[b, :, c], x[b, :, c]])
+            ref = np.correlate(u, w[c], mode="valid") + bias[c]
+            assert np.allclose(y[b, :, c], ref, rtol=1e-13, atol=1e-13), (b, c)
+
+
+def pin_conv_split_and_linearity(lib):
+    """Carrying the state across calls gives bitwise one call's result (any
+    split, one token per call included); without the activation the
+    convolution is linear in (input, state)."""
+    rng = _rng(43)
+    B, T, C, K = 2, 17, 6, 4
+    x = rng.standard_normal((B, T, C))
+    st0 = rng.standard_normal((B, K - 1, C))
+    w = rng.standard_normal((C, K))
+    bias = rng.standard_normal(C)
+    y1, s1 = oracle.causal_conv1d(x, w, bias, st0, silu=True, lib=lib)
+    for splits in ([5, 12], [1] * T, [2, 1, 14]):
+        st, ys, t0 = st0, [], 0
+        for n in splits:
+            y, st = oracle.causal_conv1d(x[:, t0:t0 + n], w, bias, st, silu=True, lib=lib)
+            ys.append(y)
+            t0 += n
+        assert np.array_equal(np.concatenate(ys, axis=1), y1) and np.array_equal(st, s1), splits
+    x2 = rng.standard_normal((B, T, C))
+    st2 = rng.standard_normal((B, K - 1, C))
+    a, b = 0.7, -1.3
+    ya, _ = oracle.causal_conv1d(x, w, None, st0, silu=False, lib=lib)
+    yb, _ = oracle.causal_conv1d(x2, w, None, st2, silu=False, lib=lib)
+    yab, _ = oracle.causal_conv1d(a * x + b * x2, w, None, a * st0 + b * st2, silu=False, lib=lib)
+    assert np.allclose(yab, a * ya + b * yb, rtol=1e-12, atol=1e-12)
+
+
+def pin_rmsnorm_closed_forms(lib):
+    """Gated RMS norm: a constant row normalises to its sign; a row of +-1
+    (unit RMS) passes through times w * silu(z); z = 0 gives zero; [3, 4]
+    has RMS sqrt(12.5); scaling a row leaves it unchanged (eps = 0); a zero
+    row stays zero for eps > 0; no gate when z is None."""
+    rng = _rng(44)
+    D = 8
+    w = rng.uniform(0.5, 1.5, D)
+    x = np.array([[-2.5] * D, [4.0] * D])
+    y = oracle.gated_rmsnorm(x, None, np.ones(D), eps=0.0, lib=lib)
+    assert np.allclose(y, np.sign(x), rtol=1e-15, atol=0)
+    x = rng.choice([-1.0, 1.0], size=(3, D))
+    z = rng.standard_normal((3, D))
+    y = oracle.gated_rmsnorm(x, z, w, eps=0.0, lib=lib)
+    assert np.allclose(y, x * w * z / (1.0 + np.exp(-z)), rtol=1e-14, atol=0)
+    assert np.array_equal(oracle.gated_rmsnorm(x, np.zeros_like(z), w, eps=1e-6, lib=lib),
+                          np.zeros_like(x))
+    y = oracle.gated_rmsnorm(np.array([[3.0, 4.0]]), None, np.ones(2), eps=0.0, lib=lib)
+    assert np.allclose(y, [[3.0 / np.sqrt(12.5), 4.0 / np.sqrt(12.5)]], rtol=1e-15, atol=0)
+    x = rng.standard_normal((4, D))
+    z = rng.standard_normal((4, D))
+    assert np.allclose(oracle.gated_rmsnorm(37.0 * x, z, w, eps=0.0, lib=lib),
+                       oracle.gated_rmsnorm(x, z, w, eps=0.0, lib=lib), rtol=1e-13, atol=0)
+    assert np.array_equal(oracle.gated_rmsnorm(np.zeros((2, D)), None, w, eps=1e-6, lib=lib),
+                          np.zeros((2, D)))
+    # eps enters under the root: a row of RMS r reads r / sqrt(r^2 + eps)
+    y = oracle.gated_rmsnorm(np.full((1, D), 0.01), None, np.ones(D), eps=1e-4, lib=lib)
+    assert np.allclose(y, 0.01 / np.sqrt(1e-4 + 1e-4), rtol=1e-14, atol=0)
+
+
 PINS = [
     pin_identity_plumbing,
     pin_matrix_form,
@@ -390,4 +505,8 @@ PINS = [
     pin_chunked_equals_sequential,
     pin_triangular_inverse,
     pin_qwen_gates,
+    pin_conv_closed_forms,
+    pin_conv_library_correlation,
+    pin_conv_split_and_linearity,
+    pin_rmsnorm_closed_forms,
 ]

@@ -60,6 +60,22 @@ MUTANTS = {
     "gate_beta_sign": [("beta[e] = 1.0 / (1.0 + exp(-b[e]));", "beta[e] = 1.0 / (1.0 + exp(b[e]));")],
     "neumann_one_factor_short": [("for (int span = 1; span < n; span *= 2) {",
                                   "for (int span = 2; span < n; span *= 2) {")],
+    "conv_kernel_reversed": [("acc += w[(size_t)c * K + j] * u[(size_t)(t + j) * C + c];",
+                              "acc += w[(size_t)c * K + (K - 1 - j)] * u[(size_t)(t + j) * C + c];")],
+    "conv_no_activation": [("y[((size_t)b * T + t) * C + c] = silu_on ? silu(acc) : acc;",
+                            "y[((size_t)b * T + t) * C + c] = acc;")],
+    "conv_state_not_carried": [("u[(size_t)i * C + c] = state_in ? state_in[((size_t)b * P + i) * C + c] : 0.0;",
+                                "u[(size_t)i * C + c] = 0.0;")],
+    "conv_state_out_shifted": [("state_out[((size_t)b * P + i) * C + c] = u[(size_t)(T + i) * C + c];",
+                                "state_out[((size_t)b * P + i) * C + c] = u[(size_t)(T - 1 + i) * C + c];")],
+    "conv_bias_dropped": [("double acc = bias ? bias[c] : 0.0;", "double acc = 0.0;")],
+    "silu_sign": [("static double silu(double x) { return x / (1.0 + exp(-x)); }",
+                   "static double silu(double x) { return x / (1.0 + exp(x)); }")],
+    "rmsnorm_sum_not_mean": [("const double inv = 1.0 / sqrt(ss / D + eps);",
+                              "const double inv = 1.0 / sqrt(ss + eps);")],
+    "rmsnorm_eps_outside_root": [("const double inv = 1.0 / sqrt(ss / D + eps);",
+                                  "const double inv = 1.0 / (sqrt(ss / D) + eps);")],
+    "rmsnorm_gate_ignored": [("const double g = z ? silu(z[r * D + i]) : 1.0;", "const double g = 1.0;")],
 }
 
 
