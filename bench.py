@@ -17,6 +17,8 @@ Also timed in the same run:
   "decode_B128"    128 sequences (403 MB of state);
   "checkpoints", "raw_gates", "varlen", "decode_multi", "decode_graph",
   "prefill_0.8b", "long_context"  (the other entry points and shapes);
+  "conv1d", "gated_rmsnorm" the causal conv1d and gated RMS norm around the
+                   recurrence at one 27B layer's shapes;
   "measured_peaks" the library's own streaming-copy and bf16 matrix-core
                    calibration kernels (include/gdn_calib.h).
 
@@ -544,6 +546,67 @@ def bench_decode_graph(torch, gdn, d, steps, warmup, chunk_steps: int = 100):
     return t["median_ms"] / chunk_steps
 
 
+def bench_conv1d(torch, gdn, steps, warmup) -> dict:
+    """Causal conv1d (width 4, SiLU, state carried) over the q, k, v
+    projections of one 27B layer: C = 2 x 16 x 128 + 48 x 128 = 10240
+    channels, prefill (B=1, T=16384) and one decode step (B=64, T=1, state
+    updated in place).  HBM-bound: x read and y written once, plus the
+    weights and states."""
+    out = {}
+    C, K = 10240, 4
+    g = torch.Generator(device="cuda").manual_seed(0)
+    w = torch.randn((C, K), device="cuda", generator=g) * 0.5
+    bias = torch.randn((C,), device="cuda", generator=g) * 0.1
+    for name, B, T in (("prefill_B1_T16384", 1, 16384), ("decode_B64_T1", 64, 1)):
+        x = torch.randn((B, T, C), device="cuda", generator=g).to(torch.bfloat16)
+        st = torch.randn((B, K - 1, C), device="cuda", generator=g).to(torch.bfloat16)
+        y = torch.empty_like(x)
+
+        def call():
+            gdn.gdn_causal_conv1d(x, w, bias, st, out=y, state_out=st)
+
+        spin_up(torch)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        t = time_calls(torch, call, steps)
+        ms = t["median_ms"]
+        nbytes = 2 * B * T * C * 2 + 2 * B * (K - 1) * C * 2 + C * (K + 1) * 4
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"us_per_call": round(ms * 1e3, 3), "algorithmic_bytes": nbytes,
+                     "GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                     "timing": timing_summary(t)}
+        log(f"conv1d {name}: {ms * 1e3:.2f} us, {gbps:.0f} GB/s")
+    return out
+
+
+def bench_rmsnorm(torch, gdn, steps, warmup) -> dict:
+    """Gated RMS norm of one 27B layer's prefill output: 16384 tokens x 48
+    value heads rows of 128 bf16 values, gate z of the same shape."""
+    rows, D = 16384 * 48, 128
+    g = torch.Generator(device="cuda").manual_seed(1)
+    x = torch.randn((rows, D), device="cuda", generator=g).to(torch.bfloat16)
+    z = torch.randn((rows, D), device="cuda", generator=g).to(torch.bfloat16)
+    w = torch.rand((D,), device="cuda", generator=g) + 0.5
+    y = torch.empty_like(x)
+
+    def call():
+        gdn.gdn_gated_rmsnorm(x, z, w, 1e-6, out=y)
+
+    spin_up(torch)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t = time_calls(torch, call, steps)
+    ms = t["median_ms"]
+    nbytes = 3 * rows * D * 2 + D * 4
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"gated rmsnorm 27B output: {ms * 1e3:.2f} us, {gbps:.0f} GB/s")
+    return {"rows": rows, "D": D, "us_per_call": round(ms * 1e3, 3), "algorithmic_bytes": nbytes,
+            "GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "timing": timing_summary(t)}
+
+
 def bench_decode(torch, gdn, d, steps, warmup, rotate: int = 1, clock=None):
     """Per-step timing of gdn_decode_step over `steps` steps of distinct inputs.
     With rotate > 1 the steps cycle over that many independent state buffers,
@@ -851,6 +914,11 @@ def main():
             "state_checkpoint_bank_bytes": ncalls * pl.B * pl.Hv * pl.dk * pl.dv * 4,
         }
         log(f"long context: {ms_l:.3f} ms per prompt, {ms_l * 1e3 / ncalls:.1f} us per call")
+
+    if args.only in ("all", "prefill") and not args.no_extras:
+        # the operations around the recurrence, at the 27B layer's shapes
+        result["conv1d"] = bench_conv1d(torch, gdn, steps, args.warmup)
+        result["gated_rmsnorm"] = bench_rmsnorm(torch, gdn, steps, args.warmup)
 
     if args.only == "decode_rot":
         # profiling: the past-cache decode leg alone (4 state buffers cycled)

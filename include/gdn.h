@@ -283,6 +283,53 @@ gdn_status gdn_chunk_prefill_noalloc(const gdn_problem* problem,
 size_t gdn_chunk_prefill_noalloc_max_workspace(void);
 
 /*
+ * The operations around the recurrence.  "Qwen3.5 Gated Delta Net NKI Kernel
+ * for AWS Neuron", section "How It Works", names them (projections, causal
+ * conv1d, gating, RMS norm) without formulas, and "Add Qwen3.6-27B hybrid
+ * DeltaNet/GQA contrib model and vLLM serving path", section "Summary",
+ * checkpoints the convolution state beside the recurrent one.  These are the
+ * plain readings of the two that are not projections.
+ *
+ * gdn_causal_conv1d: depthwise causal convolution over the channel axis of
+ * the q, k, v projections (before the recurrence), width K,
+ *   y[b,t,c] = act(bias[c] + sum_{j=0}^{K-1} w[c,j] u[b, t-K+1+j, c]),
+ * act = SiLU (x / (1 + e^-x)) when silu != 0, else identity; u is x after the
+ * carried state: u[b, s, c] = x[b, s, c] for s >= 0, state_in[b, K-1+s, c]
+ * for s < 0 (zeros when state_in is NULL).  The new state is the last K-1
+ * inputs, state_out[b, i, c] = u[b, T-K+1+i, c].
+ *   x, y              [B, T, C]    dtype (gdn_dtype: fp32 or bf16)
+ *   weight            [C, K]       fp32; bias [C] fp32 or NULL
+ *   state_in/out      [B, K-1, C]  dtype; either may be NULL; state_out may
+ *                                  be state_in itself (updated in place)
+ * 1 <= K <= 4; C * sizeof(dtype) a multiple of 16; T = 0 only writes the
+ * state; at most 65535 x 64 tokens per call and 65535 sequences.  Consecutive
+ * calls carrying the state give bitwise the result of one call.  fp32
+ * arithmetic, outputs rounded to the dtype.  y may not overlap any input;
+ * state_out may not overlap x, y, weight or bias.
+ * Errors: GDN_ERR_UNSUPPORTED (dtype, K, C), GDN_ERR_BAD_SHAPE,
+ * GDN_ERR_NULL_POINTER, GDN_ERR_MISALIGNED, GDN_ERR_ALIAS, GDN_ERR_HIP.
+ */
+gdn_status gdn_causal_conv1d(int32_t B, int32_t T, int32_t C, int32_t K, int32_t dtype,
+                             const void* x, const float* weight, const float* bias,
+                             const void* state_in, void* state_out, void* y, int32_t silu,
+                             void* hip_stream);
+
+/*
+ * gdn_gated_rmsnorm: the RMS norm and output gate of the recurrence's output,
+ * per row of D values (a row = one token of one value head, D = dv):
+ *   y[r, i] = x[r, i] / sqrt(mean_i x[r, i]^2 + eps) * weight[i] * silu(z[r, i])
+ * (z NULL: no gate).  x, z, y [rows, D] dtype; weight [D] fp32.  D / (16 /
+ * sizeof(dtype)) must be a power of two from 2 to 64 (bf16: D = 16 .. 512;
+ * fp32: 8 .. 256); rows < 2^32.  y may be x itself (in place); y may not
+ * overlap z or weight.  fp32 arithmetic, the row's sum of squares reduced in
+ * a fixed order (deterministic).
+ * Errors: GDN_ERR_UNSUPPORTED (dtype, D), GDN_ERR_BAD_SHAPE (rows, eps < 0),
+ * GDN_ERR_NULL_POINTER, GDN_ERR_MISALIGNED, GDN_ERR_ALIAS, GDN_ERR_HIP.
+ */
+gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t D, int32_t dtype, const void* x, const void* z,
+                             const float* weight, float eps, void* y, void* hip_stream);
+
+/*
  * Multi-token decode: problem->T >= 0 tokens per sequence applied in order to
  * a state that stays on chip for the whole call, for speculative or
  * multi-token-prediction verification and small continuous-batching steps

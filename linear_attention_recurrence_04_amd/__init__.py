@@ -6,7 +6,8 @@ generator (``.inputs``) imports on machines without a GPU; a call without the
 built library raises.
 """
 from .binding import (GDN_DTYPE_BF16, GDN_DTYPE_F32, GdnError, GdnProblem,  # noqa: F401
-                      gdn_abi_version, gdn_calib_copy, gdn_calib_mfma_loop,
+                      gdn_abi_version, gdn_calib_copy, gdn_calib_mfma_loop, gdn_causal_conv1d,
+                      gdn_gated_rmsnorm,
                       gdn_chunk_prefill, gdn_chunk_prefill_ckpt,
                       gdn_chunk_prefill_gated, gdn_decode_step_gated, gdn_decode_multi,
                       gdn_chunk_prefill_varlen, gdn_chunk_prefill_onchip,

@@ -93,6 +93,11 @@ def _declare(L):
     L.gdn_chunk_prefill_noalloc.argtypes = [pp, vp, vp, vp, fp, fp, fp, fp, vp, vp]
     L.gdn_chunk_prefill_noalloc_max_workspace.restype = sz
     L.gdn_chunk_prefill_noalloc_max_workspace.argtypes = []
+    L.gdn_causal_conv1d.restype = ctypes.c_int
+    L.gdn_causal_conv1d.argtypes = [ctypes.c_int32] * 5 + [vp, fp, fp, vp, vp, vp, ctypes.c_int32, vp]
+    L.gdn_gated_rmsnorm.restype = ctypes.c_int
+    L.gdn_gated_rmsnorm.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, fp,
+                                    ctypes.c_float, vp, vp]
     # calibration kernels (include/gdn_calib.h)
     L.gdn_calib_copy.restype = ctypes.c_int
     L.gdn_calib_copy.argtypes = [vp, vp, sz, ctypes.c_int32, vp]
@@ -574,6 +579,63 @@ def gdn_chunk_prefill_noalloc(q, k, v, log_g, beta, h0=None, *, chunk: int = 64,
                                          _stream(stream))
     _check(st)
     return out, hT
+
+
+@_on_stream
+def gdn_causal_conv1d(x, weight, bias=None, state_in=None, *, silu: bool = True, out=None,
+                      state_out=None, want_state: bool = True, stream=None):
+    """Causal depthwise conv1d over the channel axis.  x [B, T, C] (bf16 or
+    fp32), weight [C, K] fp32, bias [C] fp32 or None, state_in [B, K-1, C] or
+    None (zeros).  Returns (y [B, T, C], state_out [B, K-1, C] or None);
+    ``state_out`` may be ``state_in`` to update it in place."""
+    torch = _torch()
+    _need(x, "x")
+    dt = _dtype_code(x)
+    B, T, C = x.shape
+    _need(weight, "weight", torch.float32)
+    if weight.dim() != 2 or weight.shape[0] != C:
+        raise ValueError("weight must be [C, K]")
+    K = weight.shape[1]
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (C,))
+    if state_in is not None:
+        _need(state_in, "state_in", x.dtype, (B, K - 1, C))
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _need(out, "out", x.dtype, (B, T, C))
+    if state_out is None and want_state:
+        state_out = torch.empty((B, K - 1, C), dtype=x.dtype, device=x.device)
+    elif state_out is not None:
+        _need(state_out, "state_out", x.dtype, (B, K - 1, C))
+    st_ptr = _ptr(state_out) if state_out is not None and state_out.numel() else None
+    _check(lib().gdn_causal_conv1d(B, T, C, K, dt, _ptr(x) if x.numel() else None, _ptr(weight),
+                                   _ptr(bias), _ptr(state_in) if state_in is not None and state_in.numel() else None,
+                                   st_ptr, _ptr(out) if out.numel() else None, int(bool(silu)),
+                                   _stream(stream)))
+    return out, state_out
+
+
+@_on_stream
+def gdn_gated_rmsnorm(x, z, weight, eps: float = 1e-6, *, out=None, stream=None):
+    """y = x / sqrt(mean(x^2) + eps) * weight * silu(z) over the last axis of x
+    (bf16 or fp32); z like x or None (no gate); weight fp32 [D].  ``out`` may
+    be x itself."""
+    torch = _torch()
+    _need(x, "x")
+    dt = _dtype_code(x)
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    if z is not None:
+        _need(z, "z", x.dtype, tuple(x.shape))
+    _need(weight, "weight", torch.float32, (D,))
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _need(out, "out", x.dtype, tuple(x.shape))
+    _check(lib().gdn_gated_rmsnorm(rows, D, dt, _ptr(x) if rows else None, _ptr(z) if z is not None and rows else None,
+                                   _ptr(weight), float(eps), _ptr(out) if rows else None, _stream(stream)))
+    return out
 
 
 # ---------------------------------------------------------------------------

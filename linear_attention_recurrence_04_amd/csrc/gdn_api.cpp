@@ -343,3 +343,63 @@ gdn_status gdn_decode_step_gated(const gdn_problem* p, const void* q, const void
 }
 
 }  // extern "C"
+
+extern "C" {
+
+gdn_status gdn_causal_conv1d(int32_t B, int32_t T, int32_t C, int32_t K, int32_t dtype,
+                             const void* x, const float* weight, const float* bias,
+                             const void* state_in, void* state_out, void* y, int32_t silu,
+                             void* hip_stream) {
+    if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+    if (K < 1 || K > 4) return GDN_ERR_UNSUPPORTED;
+    if (B < 0 || T < 0 || C <= 0) return GDN_ERR_BAD_SHAPE;
+    const size_t es = dtype == GDN_DTYPE_BF16 ? 2 : 4;
+    if ((C * es) % 16 != 0) return GDN_ERR_UNSUPPORTED;
+    if ((T + gdn::kConvTileTokens - 1) / gdn::kConvTileTokens > 65535 || B > 65535)
+        return GDN_ERR_BAD_SHAPE;   // grid limits: token tiles (y), sequences (z)
+    const size_t xy_bytes = (size_t)B * T * C * es;
+    const size_t st_bytes = (size_t)B * (K - 1) * C * es;
+    if (!weight) return GDN_ERR_NULL_POINTER;
+    if (xy_bytes > 0 && (!x || !y)) return GDN_ERR_NULL_POINTER;
+    const void* ptrs[] = {x, weight, bias, state_in, state_out, y};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
+    const Range r_x = range_of(x, xy_bytes), r_y = range_of(y, xy_bytes);
+    const Range r_w = range_of(weight, (size_t)C * K * 4), r_b = range_of(bias, bias ? (size_t)C * 4 : 0);
+    const Range r_si = range_of(state_in, state_in ? st_bytes : 0);
+    const Range r_so = range_of(state_out, state_out ? st_bytes : 0);
+    const Range ins[] = {r_x, r_w, r_b, r_si};
+    for (const Range& in : ins)
+        if (overlaps(in, r_y)) return GDN_ERR_ALIAS;
+    if (overlaps(r_so, r_y) || overlaps(r_so, r_x) || overlaps(r_so, r_w) || overlaps(r_so, r_b))
+        return GDN_ERR_ALIAS;
+    if (state_in && state_out && state_in != state_out && overlaps(r_si, r_so)) return GDN_ERR_ALIAS;
+    gdn::ConvArgs a{B, T, C, K, dtype == GDN_DTYPE_BF16, x, weight, bias, state_in, state_out, y,
+                    silu ? 1 : 0};
+    const hipError_t err = gdn::launch_causal_conv1d(a, static_cast<hipStream_t>(hip_stream));
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t D, int32_t dtype, const void* x, const void* z,
+                             const float* weight, float eps, void* y, void* hip_stream) {
+    if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return GDN_ERR_UNSUPPORTED;
+    if (rows < 0 || D <= 0 || !(eps >= 0.f)) return GDN_ERR_BAD_SHAPE;
+    if (!gdn::conv_norm_dim_supported(D, dtype == GDN_DTYPE_BF16)) return GDN_ERR_UNSUPPORTED;
+    if (rows >= ((int64_t)1 << 32)) return GDN_ERR_BAD_SHAPE;   // grid limit (blocks of 256 lanes)
+    if (!weight) return GDN_ERR_NULL_POINTER;
+    const size_t es = dtype == GDN_DTYPE_BF16 ? 2 : 4;
+    const size_t bytes = (size_t)rows * D * es;
+    if (bytes > 0 && (!x || !y)) return GDN_ERR_NULL_POINTER;
+    const void* ptrs[] = {x, z, weight, y};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
+    const Range r_x = range_of(x, bytes), r_y = range_of(y, bytes);
+    const Range r_z = range_of(z, z ? bytes : 0), r_w = range_of(weight, (size_t)D * 4);
+    if (overlaps(r_z, r_y) || overlaps(r_w, r_y)) return GDN_ERR_ALIAS;
+    if (x != y && overlaps(r_x, r_y)) return GDN_ERR_ALIAS;
+    gdn::NormArgs a{rows, D, dtype == GDN_DTYPE_BF16, x, z, weight, eps, y};
+    const hipError_t err = gdn::launch_gated_rmsnorm(a, static_cast<hipStream_t>(hip_stream));
+    return err == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // extern "C"

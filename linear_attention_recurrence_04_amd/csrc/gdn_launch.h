@@ -59,6 +59,37 @@ hipError_t launch_prefill_fused(const PrefillArgs& a, hipStream_t stream);
 // hT = h0 (or zeros) without touching anything else (T == 0).
 hipError_t launch_state_copy(const float* h0, float* hT, size_t n, hipStream_t stream);
 
+// Causal depthwise conv1d over [B, T, C] with the last K-1 inputs carried
+// (C a multiple of 16 bytes of the dtype, 1 <= K <= 4).  Grid: x channel
+// groups, y tiles of kConvTileTokens tokens (at most 65535), z sequences.
+constexpr int kConvTileTokens = 64;
+struct ConvArgs {
+    int B, T, C, K;
+    bool bf16;
+    const void* x;          // [B, T, C]
+    const float* w;         // [C, K]
+    const float* bias;      // [C] or null
+    const void* state_in;   // [B, K-1, C] or null (zeros)
+    void* state_out;        // [B, K-1, C] or null; may be state_in
+    void* y;                // [B, T, C]
+    int silu;
+};
+hipError_t launch_causal_conv1d(const ConvArgs& a, hipStream_t stream);
+
+// y = x / sqrt(mean(x^2) + eps) * w * silu(z) per row of D values.
+struct NormArgs {
+    long long rows;
+    int D;
+    bool bf16;
+    const void* x;          // [rows, D]
+    const void* z;          // [rows, D] or null (no gate)
+    const float* w;         // [D]
+    float eps;
+    void* y;                // [rows, D]; may be x
+};
+bool conv_norm_dim_supported(int D, bool bf16);
+hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t stream);
+
 // gdn_chunk_prefill's checks and dispatch with the workspace given by the
 // caller of this function (gdn_api.cpp); returns a gdn_status value.
 int prefill_checked(const void* problem, const void* q, const void* k, const void* v,

@@ -264,3 +264,38 @@ def test_noalloc_prefill_refuses_before_any_device_call():
     assert L.gdn_chunk_prefill_noalloc(ctypes.byref(big2), *args) == 5
     bad = B.make_problem(1, 64, 16, 40, 128, 128)          # Hv % Hk != 0
     assert L.gdn_chunk_prefill_noalloc(ctypes.byref(bad), *args) == 2
+
+
+def test_conv1d_and_rmsnorm_reject_bad_arguments():
+    """The conv1d and gated RMS norm entry points check on the host and
+    enqueue nothing when they refuse (fake addresses, never dereferenced)."""
+    L = B.lib()
+    a, w, y, s1, s2 = 1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20
+    bf16, f32 = 1, 0
+    conv = L.gdn_causal_conv1d
+    assert conv(1, 10, 64, 4, 7, a, w, None, None, None, y, 1, None) == 3       # dtype
+    assert conv(1, 10, 64, 5, bf16, a, w, None, None, None, y, 1, None) == 3    # K
+    assert conv(1, 10, 60, 4, bf16, a, w, None, None, None, y, 1, None) == 3    # C * 2 % 16
+    assert conv(1, 10, 6, 4, f32, a, w, None, None, None, y, 1, None) == 3      # C * 4 % 16
+    assert conv(-1, 10, 64, 4, bf16, a, w, None, None, None, y, 1, None) == 2
+    assert conv(1, 65535 * 64 + 1, 64, 4, bf16, a, w, None, None, None, y, 1, None) == 2
+    assert conv(1, 10, 64, 4, bf16, None, w, None, None, None, y, 1, None) == 1
+    assert conv(1, 10, 64, 4, bf16, a, None, None, None, None, y, 1, None) == 1
+    assert conv(1, 10, 64, 4, bf16, a + 8, w, None, None, None, y, 1, None) == 4
+    assert conv(1, 10, 64, 4, bf16, a, w, None, None, None, a + 256, 1, None) == 7   # y over x
+    assert conv(1, 10, 64, 4, bf16, a, w, None, s1, s1 + 64, y, 1, None) == 7      # states overlap
+    assert conv(1, 10, 64, 4, bf16, a, w, None, s1, y + 64, y, 1, None) == 7       # state_out inside y
+    assert conv(0, 10, 64, 4, bf16, None, w, None, None, None, None, 1, None) == 0  # nothing to do
+    norm = L.gdn_gated_rmsnorm
+    assert norm(10, 128, 7, a, None, w, 1e-6, y, None) == 3
+    assert norm(10, 120, bf16, a, None, w, 1e-6, y, None) == 3     # D / 8 not a power of two
+    assert norm(10, 1024, bf16, a, None, w, 1e-6, y, None) == 3    # D / 8 > 64
+    assert norm(10, 8, bf16, a, None, w, 1e-6, y, None) == 3       # one lane per row
+    assert norm(-1, 128, bf16, a, None, w, 1e-6, y, None) == 2
+    assert norm(10, 128, bf16, a, None, w, -1.0, y, None) == 2
+    assert norm(10, 128, bf16, a, None, None, 1e-6, y, None) == 1
+    assert norm(10, 128, bf16, None, None, w, 1e-6, y, None) == 1
+    assert norm(10, 128, bf16, a, s1, w, 1e-6, s1 + 16, None) == 7  # y over z
+    assert norm(10, 128, bf16, a, None, w, 1e-6, a + 16, None) == 7  # y partly over x
+    assert norm(10, 128, bf16, a + 4, None, w, 1e-6, y, None) == 4
+    assert norm(0, 128, bf16, None, None, w, 1e-6, None, None) == 0
