@@ -41,6 +41,7 @@
 //    waves stream the inputs into double-buffered LDS with direct
 //    global -> LDS loads.
 #include "prefill_mfma_common.h"
+#include <type_traits>
 
 namespace gdn {
 namespace mfma_prefill {
@@ -348,9 +349,14 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
 #pragma unroll
             for (int a = 0; a < 8; ++a) S[a] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        for (int c = 0; c <= NTb; ++c) {
+        // one chunk; the buffer indices (c % 3, c % 2) are compile-time
+        // constants, so that every LDS address is a fixed lane offset plus
+        // an immediate
+        auto chunk_step = [&](auto kbuf, auto xbuf, int c) __attribute__((always_inline)) {
+            constexpr int KB = decltype(kbuf)::value;
+            constexpr int XB = decltype(xbuf)::value;
             if (c < NTb) {
-                const KSet& B = sm.ks[c % 3];
+                const KSet& B = sm.ks[KB];
                 // ---- K operands of the first k step, then the bf16 state
                 //      operands (also left in LDS for the output wave)
                 bf16x8 ak[4];
@@ -360,7 +366,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     SB[ks] = pack8(S[2 * ks], S[2 * ks + 1]);
-                    sm.Sx[c & 1][strip][ks][lane] = SB[ks];   // for the output wave
+                    sm.Sx[XB][strip][ks][lane] = SB[ks];   // for the output wave
                 }
                 // ---- K S: k step outer, 4 independent accumulators inner.  The
                 //      v values, Gamma rk, beta and the T operands, needed only
@@ -456,8 +462,8 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 for (int a = 0; a < 8; ++a) akt[a][1] = ldkt(a, 1);
                 __builtin_amdgcn_sched_barrier(0);
                 // ---- Delta operands: plain (to the output wave) and scaled (state update)
-                sm.Dx[c & 1][strip][0][lane] = pack8(Dl[0], Dl[1]);
-                sm.Dx[c & 1][strip][1][lane] = pack8(Dl[2], Dl[3]);
+                sm.Dx[XB][strip][0][lane] = pack8(Dl[0], Dl[1]);
+                sm.Dx[XB][strip][1][lane] = pack8(Dl[2], Dl[3]);
                 const bf16x8 DWB0 = pack8(Dl[0] * wg[0], Dl[1] * wg[1]);
                 const bf16x8 DWB1 = pack8(Dl[2] * wg[2], Dl[3] * wg[3]);
                 // ---- state update S <- Gamma_C S + K^T (wrk Delta), 8 independent tiles
@@ -480,6 +486,17 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 }
             }
             __syncthreads();
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        for (int c = 0; c <= NTb; c += 6) {
+            chunk_step(I0{}, I0{}, c);
+            if (c + 1 <= NTb) chunk_step(I1{}, I1{}, c + 1);
+            if (c + 2 <= NTb) chunk_step(I2{}, I0{}, c + 2);
+            if (c + 3 <= NTb) chunk_step(I0{}, I1{}, c + 3);
+            if (c + 4 <= NTb) chunk_step(I1{}, I0{}, c + 4);
+            if (c + 5 <= NTb) chunk_step(I2{}, I1{}, c + 5);
         }
         if (hT) {
             float* hp = hT + state_base + jw + n;
