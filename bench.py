@@ -487,8 +487,9 @@ def measured_peaks(torch, gdn, calls: int = 20):
     res["hbm_copy_GBps"] = res["copy_hbm_2GiB_GBps"]
     res["note"] = ("in-library kernels: streaming copy (bytes read + written; 1, 4 or 2 "
                    "16-byte accesses per thread, the last non-temporal) and a loop of 8 "
-                   "independent v_mfma_f32_16x16x32_bf16 / 32x32x16_bf16 chains per wave on "
-                   f"{wgs} workgroups of 4 waves; medians of {calls} launches, best variant")
+                   "v_mfma_f32_16x16x32_bf16 (one accumulator chain) / 32x32x16_bf16 (8 "
+                   f"independent chains) per wave and iteration on {wgs} workgroups of 4 waves; "
+                   f"medians of {calls} launches, best variant")
     return res
 
 

@@ -7,8 +7,8 @@
  *   gdn_calib_copy       a streaming device-to-device copy (HBM bandwidth:
  *                        every byte read once and written once);
  *   gdn_calib_mfma_loop  dense bf16 matrix-core work with no memory traffic
- *                        (independent chains of v_mfma_f32_16x16x32_bf16 or
- *                        v_mfma_f32_32x32x16_bf16 on register operands).
+ *                        (v_mfma_f32_16x16x32_bf16 or v_mfma_f32_32x32x16_bf16
+ *                        on register operands).
  *
  * Neither is part of the gated-delta-rule computation.  Conventions are those
  * of gdn.h: device pointers, the caller's stream (NULL = the null stream), no
@@ -40,11 +40,16 @@ gdn_status gdn_calib_copy(const void* src, void* dst, size_t bytes, int32_t vari
                           void* hip_stream);
 
 /* Run `workgroups` workgroups of 256 threads (4 waves); every wave issues
- * iters x 8 matrix-core instructions in 8 independent accumulator chains and
- * stores one float (the sum of its accumulators) to out[4 * wg + wave]
- * (out: workgroups * 4 floats, device memory, 16-byte aligned).
- *   variant 0  v_mfma_f32_16x16x32_bf16: 2*16*16*32 = 16384 flops each;
- *   variant 1  v_mfma_f32_32x32x16_bf16: 2*32*32*16 = 32768 flops each.
+ * iters x 8 matrix-core instructions and stores one float (the sum of its
+ * accumulators) to out[4 * wg + wave] (out: workgroups * 4 floats, device
+ * memory, 16-byte aligned).
+ *   variant 0  v_mfma_f32_16x16x32_bf16: 2*16*16*32 = 16384 flops each, one
+ *              accumulator chain per wave (on gfx950 a dependent 16x16x32
+ *              issues back to back; several independent 4-register chains
+ *              make the compiler rotate accumulators with register moves
+ *              that then dominate the loop);
+ *   variant 1  v_mfma_f32_32x32x16_bf16: 2*32*32*16 = 32768 flops each, 8
+ *              independent accumulator chains per wave.
  * Total flops = workgroups * 4 * iters * 8 * (flops per instruction).
  * Errors: GDN_ERR_NULL_POINTER, GDN_ERR_MISALIGNED, GDN_ERR_BAD_SHAPE
  * (workgroups < 1 or iters < 1), GDN_ERR_UNSUPPORTED (variant), GDN_ERR_HIP. */

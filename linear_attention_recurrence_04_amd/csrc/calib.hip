@@ -55,8 +55,11 @@ static hipError_t launch_copy(const void* src, void* dst, size_t n16, hipStream_
 
 constexpr int kChains = 8;
 
-// Eight independent accumulator chains per wave on register operands; the
-// wave's accumulators are summed and stored once so the work stays live.
+// Eight matrix-core instructions per wave and iteration on register operands:
+// one accumulator chain for 16x16x32 (VARIANT 0; several 4-register chains
+// make the compiler rotate accumulators with register moves that then bound
+// the loop), eight independent chains for 32x32x16 (VARIANT 1).  The wave's
+// accumulators are summed and stored once so the work stays live.
 template <int VARIANT>
 __global__ __launch_bounds__(256) void mfma_loop_kernel(float* __restrict__ out, int iters) {
     const int lane = threadIdx.x & 63;
@@ -68,16 +71,12 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float* __restrict__ out,
     }
     float total = 0.f;
     if constexpr (VARIANT == 0) {
-        f32x4 acc[kChains];
-#pragma unroll
-        for (int c = 0; c < kChains; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int i = 0; i < iters; ++i) {
 #pragma unroll
-            for (int c = 0; c < kChains; ++c)
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+            for (int c = 0; c < kChains; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
         }
-#pragma unroll
-        for (int c = 0; c < kChains; ++c) total += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+        total = acc[0] + acc[1] + acc[2] + acc[3];
     } else {
         f32x16 acc[kChains];
 #pragma unroll
