@@ -449,7 +449,39 @@ def bench_long_context(torch, gdn, p, warmup):
         prompt()
     torch.cuda.synchronize()
     log(f"long context: timing 5 prompts of {ncalls} calls")
-    return time_calls(torch, prompt, 5), ncalls
+    t_calls = time_calls(torch, prompt, 5)
+    prompt()
+    torch.cuda.synchronize()
+
+    # the same prompt as ONE call: it runs in pieces of 256 chunks that reuse
+    # the documented workspace, and must end in bitwise the state and last
+    # outputs of the 256 calls (every chunk computes the same either way)
+    log("long context: the same prompt as one call")
+    full = {n: torch.cat([segs[c % LONG_DISTINCT_SEGMENTS][n] for c in range(ncalls)], dim=1)
+            for n in ("q", "k", "v", "log_g", "beta")}
+    prob1 = gdn.make_problem(p.B, p.T, p.Hk, p.Hv, p.dk, p.dv, chunk=p.chunk)
+    ws1_bytes = gdn.gdn_chunk_prefill_workspace_bytes(prob1)
+    ws1 = torch.empty(ws1_bytes, dtype=torch.uint8, device="cuda")
+    out1 = torch.empty((p.B, p.T, p.Hv, p.dv), dtype=torch.bfloat16, device="cuda")
+    h1 = torch.empty((p.B, p.Hv, p.dk, p.dv), dtype=torch.float32, device="cuda")
+
+    def one_call():
+        gdn.gdn_chunk_prefill(full["q"], full["k"], full["v"], full["log_g"], full["beta"], None,
+                              chunk=p.chunk, out=out1, hT=h1, workspace=ws1)
+
+    for _ in range(2):
+        one_call()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(h1, bank[ncalls - 1]) and torch.equal(out1[:, p.T - Tc:], out))
+    t_one = time_calls(torch, one_call, 5)
+    chunks = (p.T + p.chunk - 1) // p.chunk
+    one = {"ms_per_prompt": round(t_one["median_ms"], 4),
+           "tokens_per_s": round(p.B * p.T / (t_one["median_ms"] * 1e-3), 1),
+           "workspace_bytes": ws1_bytes, "pieces": -(-chunks // 256),
+           "bitwise_equal_to_the_calls": same}
+    del full, ws1, out1, h1
+    torch.cuda.empty_cache()
+    return t_calls, ncalls, one
 
 def measured_peaks(torch, gdn, calls: int = 20):
     """What this GPU sustains, from the library's own calibration kernels
@@ -905,7 +937,7 @@ def main():
         log(f"0.8B prefill: {ms_8 * 1e3:.1f} us/call")
         # the long prompt: 256 consecutive 512-token calls, state carried and checkpointed
         pl = gi.QWEN27B_LONG
-        t_l, ncalls = bench_long_context(torch, gdn, pl, args.warmup)
+        t_l, ncalls, one_call = bench_long_context(torch, gdn, pl, args.warmup)
         ms_l = t_l["median_ms"]
         result["long_context"] = {
             "workload": pl.name, "calls": ncalls, "tokens_per_call": pl.extra["call_tokens"],
@@ -913,6 +945,7 @@ def main():
             "ms_per_prompt": round(ms_l, 4), "us_per_call": round(ms_l * 1e3 / ncalls, 3),
             "tokens_per_s": round(pl.B * pl.T / (ms_l * 1e-3), 1),
             "state_checkpoint_bank_bytes": ncalls * pl.B * pl.Hv * pl.dk * pl.dv * 4,
+            "one_call": one_call,
         }
         log(f"long context: {ms_l:.3f} ms per prompt, {ms_l * 1e3 / ncalls:.1f} us per call")
 

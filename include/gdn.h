@@ -96,8 +96,15 @@ typedef struct {
  * the error.  The caller allocates the workspace; its contents need no
  * initialisation and are meaningless after the call.  The bf16 MFMA path
  * ("mfma_bf16" below) needs 13568 bytes per (sequence, value head, chunk of
- * 64 tokens): the chunk's triangular inverse, masked Q K^T and gate vectors,
- * computed for all chunks in parallel before the serial pass.
+ * 64 tokens) for up to 256 chunks: the chunk's triangular inverse, masked
+ * Q K^T and gate vectors, computed in parallel for a piece of chunks before
+ * the serial pass over them.  A call longer than 256 chunks runs in pieces
+ * of 256 chunks that reuse these records, and the workspace then also holds
+ * the state carried between pieces, after the records at the next multiple
+ * of 256 bytes (B * Hv * dk * dv * 4 bytes): at most
+ * 256 * 13568 * B * Hv + 255 + 65536 * B * Hv bytes whatever T.  A larger
+ * workspace is used for longer pieces; the results are bitwise the same for
+ * every piece length.
  * gdn_chunk_prefill_onchip needs no workspace.
  */
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_problem* problem);
@@ -259,11 +266,13 @@ gdn_status gdn_chunk_prefill_onchip(const gdn_problem* problem,
  * that the library holds on every GPU it runs on, from module load until the
  * process ends; the call itself allocates nothing.
  *
- *  - A problem whose gdn_chunk_prefill_workspace_bytes() exceeds that size
- *    is rejected with GDN_ERR_WORKSPACE before anything is enqueued (at the
- *    27B head shape, 48 value heads, 64 MiB covers B * T up to 6592 tokens;
- *    a longer sequence can be processed as consecutive calls carrying the
- *    state, split at multiples of the chunk: bitwise the same results).
+ *  - A call runs in pieces of as many chunks as the array holds (bitwise
+ *    the same results as gdn_chunk_prefill).  A problem for which the array
+ *    cannot hold one chunk's records (13568 * B * Hv bytes) plus, when the
+ *    call has more than one chunk, the carried state (65536 * B * Hv bytes
+ *    after the next multiple of 256) is rejected with GDN_ERR_WORKSPACE
+ *    before anything is enqueued: B * Hv up to 4946 for a one-chunk call,
+ *    up to 848 otherwise (27B head shape: 48 value heads, so B up to 17).
  *  - Every call on one GPU uses the same array and leaves its contents
  *    behind.  Calls whose kernels may overlap in time on one GPU (different
  *    streams with no ordering between them) race on it and give wrong

@@ -120,12 +120,16 @@ namespace {
 // raw gates (A_log, dt_bias non-null: log_g, beta hold the projections a, b).
 // Packed variable-length batches pass cu (device [B + 1]) and the length
 // `total` of the token axis; otherwise cu is NULL and total = B * T.
+// any_piece: accept any workspace that holds one chunk's records and the
+// carried state (the call then runs in pieces that fit), instead of the
+// size gdn_chunk_prefill_workspace_bytes documents.
 gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, const void* v,
                         const float* log_g, const float* beta, const float* A_log,
                         const float* dt_bias, const float* h0, float* hT, void* o,
                         float* h_ckpt, int ckpt_every, void* workspace,
                         size_t workspace_bytes, void* hip_stream,
-                        const int32_t* cu = nullptr, long long total = -1, bool onchip = false) {
+                        const int32_t* cu = nullptr, long long total = -1, bool onchip = false,
+                        bool any_piece = false) {
     const size_t es = dsize(p);
     if (total < 0) total = (long long)p->B * p->T;
     const size_t BT = (size_t)total;
@@ -142,7 +146,8 @@ gdn_status prefill_impl(const gdn_problem* p, const void* q, const void* k, cons
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return GDN_ERR_MISALIGNED;
 
-    const size_t need_ws = onchip ? 0 : gdn_chunk_prefill_workspace_bytes(p);
+    size_t need_ws = onchip ? 0 : gdn_chunk_prefill_workspace_bytes(p);
+    if (any_piece && need_ws > 0) need_ws = gdn::prefill_mfma_min_workspace_bytes(p->B, p->T, p->Hk, p->Hv);
     if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return GDN_ERR_WORKSPACE;
 
     // outputs against inputs: hT may be exactly h0, nothing else may overlap
@@ -197,7 +202,7 @@ int gdn::prefill_checked(const void* problem, const void* q, const void* k, cons
     const gdn_status st = check_problem(p, false);
     if (st != GDN_OK) return st;
     return prefill_impl(p, q, k, v, log_g, beta, nullptr, nullptr, h0, hT, o, nullptr, 0,
-                        workspace, workspace_bytes, hip_stream);
+                        workspace, workspace_bytes, hip_stream, nullptr, -1, false, true);
 }
 
 extern "C" {

@@ -47,9 +47,12 @@ hipError_t launch_prefill_generic(const PrefillArgs& a, hipStream_t stream);
 
 // bf16 MFMA path: bf16 inputs, head dim 128, chunk 64.  Two kernels (a
 // parallel per-chunk prep writing T, P and gates to the workspace, then the
-// serial scan over chunks).
+// serial scan over chunks), launched for pieces of at most 256 chunks (more
+// if a.ws_bytes holds them) one after the other.
 bool prefill_mfma_supported(const PrefillArgs& a);
 size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv);
+// the least workspace the bf16 MFMA prefill runs with (pieces of one chunk)
+size_t prefill_mfma_min_workspace_bytes(int B, int T, int Hk, int Hv);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
 
 // The same bf16 MFMA path (same supported shapes) in one kernel: every
@@ -91,7 +94,9 @@ bool conv_norm_dim_supported(int D, bool bf16);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t stream);
 
 // gdn_chunk_prefill's checks and dispatch with the workspace given by the
-// caller of this function (gdn_api.cpp); returns a gdn_status value.
+// caller of this function (gdn_api.cpp), which may be as small as one
+// chunk's records and the carried state (the call then runs in pieces that
+// fit); returns a gdn_status value.
 int prefill_checked(const void* problem, const void* q, const void* k, const void* v,
                     const float* log_g, const float* beta, const float* h0, float* hT, void* o,
                     void* workspace, size_t workspace_bytes, void* hip_stream);

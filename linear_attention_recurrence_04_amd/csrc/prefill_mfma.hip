@@ -122,7 +122,7 @@ __device__ __forceinline__ s16x4 ld_tr4(const void* p) {
 __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const unsigned char* __restrict__ ws, const float* h0, float* hT, bf16_t* __restrict__ o,
-    int T, int NTc, int Hk, int Hv, float q_scale, int xcd_remap,
+    int T, int NRc, int Hk, int Hv, float q_scale, int xcd_remap,
     float* __restrict__ ckpt, int ckpt_every, int nck, const int* __restrict__ cu, long long total,
     int c_first, int n_chunks) {
     __shared__ ScanSmem sm;
@@ -160,9 +160,9 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
     const int skip = min(c_first * C, Tb);
     tb0 += skip;
     Tb = min(Tb - skip, n_chunks * C);
-    const int NTb = (Tb + C - 1) / C;    // chunks to run (records are laid out for NTc)
+    const int NTb = (Tb + C - 1) / C;    // chunks to run: records 0 .. NTb - 1 of the NRc per head
     const size_t state_base = (size_t)bh * D * D;
-    const unsigned char* rec0 = ws + ((size_t)bh * NTc + c_first) * WS_REC;
+    const unsigned char* rec0 = ws + (size_t)bh * NRc * WS_REC;
     const bf16_t* kbase = k + (tb0 * Hk + hk) * D;
     const bf16_t* qbase = q + (tb0 * Hk + hk) * D;
     const bf16_t* vbase = v + (tb0 * Hv + h) * D + j0;
@@ -606,30 +606,43 @@ namespace {
 
 using namespace mfma_prefill;
 
-// Records of every (b, value head, chunk).
-size_t records_bytes(int B, int T, int Hv) {
-    const size_t NTc = (size_t)(T + C - 1) / C;
-    return (size_t)B * Hv * NTc * WS_REC;
+// A call runs in pieces of at most kPieceChunks chunks (or as many as the
+// workspace holds), each a prep launch then a scan launch on the caller's
+// stream; the records of one piece are reused by the next, and the state
+// passes from piece to piece through hT (or a slot after the records when
+// the caller wants no final state).  Every chunk computes the same whatever
+// the pieces, so the results are bitwise those of one piece.
+constexpr int kPieceChunks = 256;
+
+size_t records_bytes(int B, int Hv, int chunks) {
+    return (size_t)B * Hv * (size_t)chunks * WS_REC;
+}
+size_t carry_bytes(int B, int Hv) { return (size_t)B * Hv * D * D * sizeof(float); }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+// workspace for pieces of `piece` chunks out of NTc
+size_t workspace_for(int B, int Hv, int NTc, int piece) {
+    const int pc = piece < NTc ? piece : NTc;
+    return pc < NTc ? align256(records_bytes(B, Hv, pc)) + carry_bytes(B, Hv) : records_bytes(B, Hv, pc);
 }
 
-hipError_t launch_prep(const PrefillArgs& a, int NTc, unsigned char* ws, int c_first,
+hipError_t launch_prep(const PrefillArgs& a, int NRc, unsigned char* ws, int c_first,
                        int n_chunks, hipStream_t stream) {
-    if (a.A_log) return launch_prep_raw(a, NTc, ws, c_first, n_chunks, stream);
+    if (a.A_log) return launch_prep_raw(a, NRc, ws, c_first, n_chunks, stream);
     hipLaunchKernelGGL(chunk_prep_kernel, dim3(a.B * a.Hk * n_chunks), dim3(NT), 0, stream,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k), a.log_g,
-                       a.beta, nullptr, nullptr, ws, a.T, NTc, a.Hk, a.Hv, a.l2norm, a.cu,
+                       a.beta, nullptr, nullptr, ws, a.T, NRc, a.Hk, a.Hv, a.l2norm, a.cu,
                        a.total, c_first, n_chunks);
     return hipGetLastError();
 }
 
-hipError_t launch_scan(const PrefillArgs& a, int NTc, const unsigned char* ws, const float* h0,
+hipError_t launch_scan(const PrefillArgs& a, int NRc, const unsigned char* ws, const float* h0,
                        float* hT, int c_first, int n_chunks, hipStream_t stream) {
     const int scan_blocks = a.B * a.Hv * (D / BVS);
     const int remap = ((a.B * a.Hk) % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL(chunk_scan_kernel, dim3(scan_blocks), dim3(SNT), 0, stream,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
                        static_cast<const bf16_t*>(a.v), ws, h0, hT,
-                       static_cast<bf16_t*>(a.o), a.T, NTc, a.Hk, a.Hv, a.q_scale, remap,
+                       static_cast<bf16_t*>(a.o), a.T, NRc, a.Hk, a.Hv, a.q_scale, remap,
                        a.ckpt, a.ckpt_every, a.nck, a.cu, a.total, c_first, n_chunks);
     return hipGetLastError();
 }
@@ -638,17 +651,42 @@ hipError_t launch_scan(const PrefillArgs& a, int NTc, const unsigned char* ws, c
 
 size_t prefill_mfma_workspace_bytes(int B, int T, int Hk, int Hv) {
     (void)Hk;
-    return records_bytes(B, T, Hv);
+    return workspace_for(B, Hv, (T + C - 1) / C, kPieceChunks);
 }
 
-// The prep of every chunk, then the serial pass, both on the caller's stream.
+size_t prefill_mfma_min_workspace_bytes(int B, int T, int Hk, int Hv) {
+    (void)Hk;
+    return workspace_for(B, Hv, (T + C - 1) / C, 1);
+}
+
+// Piece by piece: the prep of the piece's chunks, then the serial pass over
+// them, on the caller's stream.  a.ws_bytes (at least the minimum above)
+// sets the piece length.
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
     const int NTc = (a.T + C - 1) / C;
     if (a.B * a.Hk * NTc == 0) return hipSuccess;
     unsigned char* ws = static_cast<unsigned char*>(a.ws);
-    const hipError_t err = launch_prep(a, NTc, ws, 0, NTc, stream);
-    if (err != hipSuccess) return err;
-    return launch_scan(a, NTc, ws, a.h0, a.hT, 0, NTc, stream);
+    int piece = NTc;
+    if (records_bytes(a.B, a.Hv, NTc) > a.ws_bytes) {
+        const size_t per = records_bytes(a.B, a.Hv, 1);
+        const size_t room = a.ws_bytes > carry_bytes(a.B, a.Hv) ? a.ws_bytes - carry_bytes(a.B, a.Hv) : 0;
+        size_t p = room / per < (size_t)NTc ? room / per : (size_t)NTc;
+        while (p > 0 && align256(records_bytes(a.B, a.Hv, (int)p)) > room) --p;
+        if (p < 1) return hipErrorInvalidValue;   // below the minimum the caller checked
+        piece = (int)p;
+    }
+    float* carry = a.hT ? a.hT : reinterpret_cast<float*>(ws + align256(records_bytes(a.B, a.Hv, piece)));
+    const float* h_in = a.h0;
+    for (int c0 = 0; c0 < NTc; c0 += piece) {
+        const int n = NTc - c0 < piece ? NTc - c0 : piece;
+        float* h_out = (c0 + n >= NTc) ? a.hT : carry;
+        hipError_t err = launch_prep(a, piece, ws, c0, n, stream);
+        if (err != hipSuccess) return err;
+        err = launch_scan(a, piece, ws, h_in, h_out, c0, n, stream);
+        if (err != hipSuccess) return err;
+        h_in = carry;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gdn

@@ -214,7 +214,7 @@ __device__ __forceinline__ void gate_tiles(PrepSmem& sm, const f32x4 (&gram)[5],
 // The prep kernel reading raw gate projections (prefill_prep_raw.hip): its
 // own translation unit, because with both prep kernels in one unit the
 // register allocator spilled in both.
-hipError_t launch_prep_raw(const PrefillArgs& a, int NTc, unsigned char* ws, int c_first,
+hipError_t launch_prep_raw(const PrefillArgs& a, int NRc, unsigned char* ws, int c_first,
                           int n_chunks, hipStream_t stream);
 
 }  // namespace mfma_prefill

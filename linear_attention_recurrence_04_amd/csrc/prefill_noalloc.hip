@@ -48,7 +48,11 @@ extern "C" gdn_status gdn_chunk_prefill_noalloc(const gdn_problem* p, const void
                                                 const float* beta, const float* h0, float* hT,
                                                 void* o, void* hip_stream) {
     if (!p) return GDN_ERR_NULL_POINTER;
-    const size_t need = gdn_chunk_prefill_workspace_bytes(p);   // 0 for an invalid problem
+    // 0 for an invalid problem (reported below) or one that needs no workspace;
+    // a call longer than the array holds runs in pieces that fit
+    const size_t need = gdn_chunk_prefill_workspace_bytes(p) > 0
+                            ? gdn::prefill_mfma_min_workspace_bytes(p->B, p->T, p->Hk, p->Hv)
+                            : 0;
     if (need > kNoallocScratchBytes) return GDN_ERR_WORKSPACE;
     void* ws = nullptr;
     if (need > 0) {

@@ -16,12 +16,12 @@ namespace mfma_prefill {
 #undef PREP_KERNEL
 #undef PREP_RAW
 
-hipError_t launch_prep_raw(const PrefillArgs& a, int NTc, unsigned char* ws, int c_first,
+hipError_t launch_prep_raw(const PrefillArgs& a, int NRc, unsigned char* ws, int c_first,
                           int n_chunks, hipStream_t stream) {
     const int blocks = a.B * a.Hk * n_chunks;
     hipLaunchKernelGGL(chunk_prep_raw_kernel, dim3(blocks), dim3(NT), 0, stream,
                        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k), a.log_g,
-                       a.beta, a.A_log, a.dt_bias, ws, a.T, NTc, a.Hk, a.Hv, a.l2norm, a.cu,
+                       a.beta, a.A_log, a.dt_bias, ws, a.T, NRc, a.Hk, a.Hv, a.l2norm, a.cu,
                        a.total, c_first, n_chunks);
     return hipGetLastError();
 }

@@ -105,14 +105,19 @@ def test_workspace_query():
 
 
 @pytest.mark.parametrize("Bn,T,Hk,Hv", [(1, 1, 1, 1), (2, 200, 1, 3), (1, 768, 16, 48),
-                                        (1, 769, 16, 48), (1, 16384, 16, 48), (3, 16400, 2, 6)])
+                                        (1, 769, 16, 48), (1, 16384, 16, 48), (1, 16385, 16, 48),
+                                        (3, 16400, 2, 6), (1, 131072, 16, 48)])
 def test_mfma_workspace_bytes_as_documented(Bn, T, Hk, Hv):
     """bf16, d = 128, chunk 64 takes the MFMA path, whose workspace is 13568
-    bytes per (sequence, value head, chunk of 64)."""
+    bytes per (sequence, value head, chunk of 64) for up to 256 chunks; a
+    longer call runs in pieces of 256 chunks and also holds the carried
+    state (65536 bytes per head) at the next multiple of 256 bytes."""
     prob = P(B=Bn, T=T, Hk=Hk, Hv=Hv, dk=128, dv=128, chunk=64, dtype=1)
     assert B.gdn_chunk_prefill_variant(prob) == "mfma_bf16"
     chunks = -(-T // 64)
-    assert B.gdn_chunk_prefill_workspace_bytes(prob) == Bn * Hv * chunks * 13568
+    want = (Bn * Hv * chunks * 13568 if chunks <= 256
+            else ((Bn * Hv * 256 * 13568 + 255) // 256) * 256 + Bn * Hv * 65536)
+    assert B.gdn_chunk_prefill_workspace_bytes(prob) == want
 
 
 def test_python_binding_refuses_cpu_tensors():
@@ -258,9 +263,11 @@ def test_noalloc_prefill_refuses_before_any_device_call():
     fake = 1 << 20
     args = [fake, fake, fake, fake, fake, None, fake, fake, None]
     assert L.gdn_chunk_prefill_noalloc(None, *args) == 1
-    big = B.make_problem(1, 6593, 16, 48, 128, 128)        # 104 chunks x 48 heads x 13568 B
+    # more than one chunk: one chunk's records and the carried state must fit,
+    # B * Hv <= 848; one chunk: the records alone, B * Hv <= 4946
+    big = B.make_problem(18, 6593, 16, 48, 128, 128)       # B * Hv = 864
     assert L.gdn_chunk_prefill_noalloc(ctypes.byref(big), *args) == 5
-    big2 = B.make_problem(2, 3400, 16, 48, 128, 128)
+    big2 = B.make_problem(104, 64, 16, 48, 128, 128)       # one chunk, B * Hv = 4992
     assert L.gdn_chunk_prefill_noalloc(ctypes.byref(big2), *args) == 5
     bad = B.make_problem(1, 64, 16, 40, 128, 128)          # Hv % Hk != 0
     assert L.gdn_chunk_prefill_noalloc(ctypes.byref(bad), *args) == 2

@@ -37,16 +37,20 @@ def test_noalloc_array_size_is_as_documented():
 
 
 def test_noalloc_matches_prefill_on_calls_in_a_row():
-    """Largest 27B-shaped call the array allows (B=1, 6592 tokens, 16/48
-    heads), then a smaller ragged call, then the largest again: each bitwise
-    equal to gdn_chunk_prefill on the same inputs."""
+    """A 27B-shaped call longer than the array holds in one piece (B=1,
+    20,000 tokens, 16/48 heads: pieces of 98 chunks), then a smaller ragged
+    call (one piece), then 35 sequences of 650 tokens over 4/20 heads (B * Hv
+    = 700: pieces of 2 chunks), then the long one again: each bitwise equal
+    to gdn_chunk_prefill on the same inputs (pieces of 256 chunks)."""
     torch = torch_mod()
-    shapes = [(1, 6592, 16, 48, 1), (2, 1100, 2, 6, 2), (1, 6592, 16, 48, 3)]
+    shapes = [(1, 20000, 16, 48, 1), (2, 1100, 2, 6, 2), (35, 650, 4, 20, 5), (1, 20000, 16, 48, 3)]
     for (B, T, Hk, Hv, seed) in shapes:
         say(f"noalloc B={B} T={T} {Hk}x{Hv} seed={seed}")
         prob = gdn.make_problem(B, T, Hk, Hv, 128, 128)
-        need = gdn.gdn_chunk_prefill_workspace_bytes(prob)
-        assert need == B * Hv * (-(-T // 64)) * REC <= MAX_WS
+        chunks = -(-T // 64)
+        one_piece = B * Hv * chunks * REC
+        assert (one_piece > MAX_WS) == (T != 1100)
+        assert B * Hv * REC + (B * Hv * 65536 if chunks > 1 else 0) <= MAX_WS
         q, k, v, lg, bt, h0 = case(B, T, Hk, Hv, seed)
         out = torch.full((B, T, Hv, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
         hT = torch.full((B, Hv, 128, 128), float("nan"), dtype=torch.float32, device="cuda")
@@ -59,10 +63,10 @@ def test_noalloc_matches_prefill_on_calls_in_a_row():
 
 
 def test_noalloc_refuses_beyond_the_array():
-    """One chunk more than fits: GDN_ERR_WORKSPACE, nothing enqueued (the
-    pointers are never used)."""
-    prob = gdn.make_problem(1, 6593, 16, 48, 128, 128)
-    assert gdn.gdn_chunk_prefill_workspace_bytes(prob) > MAX_WS
+    """One chunk's records and the carried state do not fit (B * Hv = 864):
+    GDN_ERR_WORKSPACE, nothing enqueued (the pointers are never used)."""
+    prob = gdn.make_problem(18, 6593, 16, 48, 128, 128)
+    assert 18 * 48 * (REC + 65536) > MAX_WS
     fake = 1 << 20
     st = gdn.lib().gdn_chunk_prefill_noalloc(ctypes.byref(prob), fake, fake, fake, fake, fake,
                                              None, fake, fake, None)
