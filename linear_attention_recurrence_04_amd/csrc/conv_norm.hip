@@ -24,9 +24,9 @@
 //    after it on the same stream, writes the new state (one thread per
 //    channel reads every old value it needs before writing, so the new state
 //    may overwrite the old one, also when T < K-1).
-//  * gated RMS norm: a group of D/VEC lanes per row, the sum of squares
-//    reduced by shuffles in a fixed order; each lane reads its x and z before
-//    writing y, so y may be x.
+//  * gated RMS norm: a group of D/VEC lanes per row (two rows per group),
+//    the sum of squares reduced by shuffles in a fixed order; each lane reads
+//    its x and z before writing y, so y may be x.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -226,40 +226,82 @@ hipError_t launch_conv_t(const ConvArgs& a, hipStream_t stream) {
 constexpr int NORM_THREADS = 256;
 
 // G lanes per row (D = G * N), 64 / G rows per wave
-template <typename TIn, int G>
+constexpr int NORM_ROWS = 2;   // rows per lane group
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32v4;
+
+// G lanes per row (D = G * N), NORM_ROWS rows per lane group.  Every load (x
+// and z of all its rows, then w) is issued before any arithmetic or store:
+// written in that order the compiler keeps it (y may be x, so it may not move
+// a later row's loads above an earlier row's store), and the loads are in
+// flight together.  The rows go through buffer resources on the block's rows,
+// sized to the rows that exist: a lane past the last row loads zeros and its
+// store is dropped by the hardware, so no branch guards a store (a guarded
+// store let the compiler sink the z loads into the branch, after the
+// reduction over x).  Rows are read and written with non-temporal accesses.
+// On the 27B output shape (786,432 rows of 128 bf16, gated), against one row
+// per group with plain accesses: 103 -> 91 us per call back to back, 112 ->
+// 101 us timed one call at a time.
+template <typename TIn, int G, bool GATED>
 __global__ __launch_bounds__(NORM_THREADS) void gated_rmsnorm_kernel(
     const TIn* x, const TIn* __restrict__ z, const float* __restrict__ w, float eps, TIn* y,
     long long rows) {
     constexpr int N = Vec16<TIn>::N;
     constexpr int D = G * N;
-    const long long row = ((long long)blockIdx.x * NORM_THREADS + threadIdx.x) / G;
+    constexpr int RPB = NORM_THREADS / G;   // rows of one block step
+    constexpr int BR = NORM_ROWS * RPB;     // rows of the block
     const int part = threadIdx.x % G;
-    const bool live = row < rows;
-    const long long r = live ? row : rows - 1;   // a clamped row keeps every lane in the shuffles
-    float xv[N], zv[N];
-    load16(x + r * D + part * N, xv);
-    if (z) load16(z + r * D + part * N, zv);
-    float ss = 0.f;
+    const long long row0 = (long long)blockIdx.x * BR;
+    const long long left = rows - row0;   // > 0: the grid covers the rows exactly
+    const int nrows = left < BR ? (int)left : BR;
+    const int nbytes = nrows * D * (int)sizeof(TIn);
+    const size_t base = (size_t)row0 * D;
+    const auto xs = __builtin_amdgcn_make_buffer_rsrc(const_cast<TIn*>(x) + base, (short)0, nbytes, 0x00020000);
+    const auto zs = __builtin_amdgcn_make_buffer_rsrc(const_cast<TIn*>(GATED ? z : x) + base, (short)0, nbytes,
+                                                      0x00020000);
+    const auto ys = __builtin_amdgcn_make_buffer_rsrc(y + base, (short)0, nbytes, 0x00020000);
+    int voff[NORM_ROWS];   // bytes from the block's first row
 #pragma unroll
-    for (int i = 0; i < N; ++i) ss += xv[i] * xv[i];
+    for (int j = 0; j < NORM_ROWS; ++j)
+        voff[j] = ((j * RPB + (int)threadIdx.x / G) * D + part * N) * (int)sizeof(TIn);
+    Vec16<TIn> xr[NORM_ROWS], zr[NORM_ROWS];
 #pragma unroll
-    for (int m = 1; m < G; m *= 2) ss += __shfl_xor(ss, m, 64);
-    const float inv = 1.f / sqrtf(ss / (float)D + eps);
-    float out[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const float g = z ? silu(zv[i]) : 1.f;
-        out[i] = xv[i] * inv * w[part * N + i] * g;
+    for (int j = 0; j < NORM_ROWS; ++j) {
+        xr[j] = __builtin_bit_cast(Vec16<TIn>, __builtin_amdgcn_raw_buffer_load_b128(xs, voff[j], 0, 2));
+        if constexpr (GATED)
+            zr[j] = __builtin_bit_cast(Vec16<TIn>, __builtin_amdgcn_raw_buffer_load_b128(zs, voff[j], 0, 2));
     }
-    if (live) store16(y + r * D + part * N, out);
+    float wv[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) wv[i] = w[part * N + i];
+#pragma unroll
+    for (int j = 0; j < NORM_ROWS; ++j) {
+        float xv[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) xv[i] = to_f32(xr[j].v[i]);
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) ss += xv[i] * xv[i];
+#pragma unroll
+        for (int m = 1; m < G; m *= 2) ss += __shfl_xor(ss, m, 64);
+        const float inv = 1.f / sqrtf(ss / (float)D + eps);
+        Vec16<TIn> o;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const float g = GATED ? silu(to_f32(zr[j].v[i])) : 1.f;
+            o.v[i] = from_f32<TIn>(xv[i] * inv * wv[i] * g);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4, o), ys, voff[j], 0, 2);
+    }
 }
 
 template <typename TIn, int G>
 hipError_t launch_norm_g(const NormArgs& a, hipStream_t stream) {
-    const long long threads = a.rows * G;
-    const long long blocks = (threads + NORM_THREADS - 1) / NORM_THREADS;
-    hipLaunchKernelGGL((gated_rmsnorm_kernel<TIn, G>), dim3((unsigned)blocks), dim3(NORM_THREADS), 0,
-                       stream, static_cast<const TIn*>(a.x), static_cast<const TIn*>(a.z), a.w, a.eps,
+    const long long groups = (a.rows + NORM_THREADS / G - 1) / (NORM_THREADS / G);
+    const long long blocks = (groups + NORM_ROWS - 1) / NORM_ROWS;
+    const auto kern = a.z ? gated_rmsnorm_kernel<TIn, G, true> : gated_rmsnorm_kernel<TIn, G, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NORM_THREADS), 0, stream,
+                       static_cast<const TIn*>(a.x), static_cast<const TIn*>(a.z), a.w, a.eps,
                        static_cast<TIn*>(a.y), a.rows);
     return hipGetLastError();
 }
