@@ -41,7 +41,8 @@
 // (partial rows scatter the accesses) and plain accesses were all slower.
 // Plain accesses keep a state that fits the Infinity Cache resident from step
 // to step (6.5 TB/s at B=64 on one buffer), which a model never sees.
-// Several tokens per call and head dim 64 use 256 threads and plain accesses.
+// Several tokens per call use 256 threads (non-temporal state at head dim
+// 128); a single step at head dim 64 uses 256 threads and plain accesses.
 #include <algorithm>
 
 #include "gdn_device.h"
@@ -277,8 +278,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 
 
         if (MULTI) {   // the state back over the same addresses
 #pragma unroll
-            for (int i = 0; i < RPT; ++i)
-                *reinterpret_cast<float4*>(S + (size_t)(rg + RG * i) * D + 4 * cg) = s[i];
+            for (int i = 0; i < RPT; ++i) store_state<NTS>(S + (size_t)(rg + RG * i) * D + 4 * cg, s[i]);
         }
     } while (!MULTI && (unit += gridDim.x) < units);
 }
@@ -316,7 +316,10 @@ static hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
         else
             return launch_single<D, TIn, 256, D, 0>(a, stream);
     }
-    hipLaunchKernelGGL((decode_step_kernel<D, TIn, true, 256, D, 0>), dim3(heads), dim3(256), 0, stream,
+    // several tokens per call: 256 threads per head (1024 threads, the single
+    // step's form, ran twice as long: the per-token barriers and reductions
+    // dominate), non-temporal state at head dim 128 (2-4% faster)
+    hipLaunchKernelGGL((decode_step_kernel<D, TIn, true, 256, D, D == 128 ? 3 : 0>), dim3(heads), dim3(256), 0, stream,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.v), a.log_g, a.beta, a.A_log, a.dt_bias, a.state,
                        static_cast<TIn*>(a.o), a.states, a.T, a.Hk, a.Hv, a.l2norm, a.q_scale, heads);
