@@ -56,6 +56,8 @@ FP32_VALU_PEAK_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
 # the single-step decode kernel at head dim 128 (1024 threads, non-temporal state)
 DECODE_KERNEL = "decode_step_kernel<128,bf16,false,1024,128,3>"
+CONV_KERNEL = "conv1d_kernel<bf16,4>+conv_state_kernel 27B prefill"
+NORM_KERNEL = "gated_rmsnorm_kernel<bf16,16,gated> 27B output"
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_04_amd", "csrc")
 
 
@@ -609,6 +611,8 @@ def bench_conv1d(torch, gdn, steps, warmup) -> dict:
         out[name] = {"us_per_call": round(ms * 1e3, 3), "algorithmic_bytes": nbytes,
                      "GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                      "timing": timing_summary(t)}
+        if T > 1:
+            out[name]["traffic"] = pmc_traffic(CONV_KERNEL, source_hash("conv_norm.hip", "gdn_device.h"))
         log(f"conv1d {name}: {ms * 1e3:.2f} us, {gbps:.0f} GB/s")
     return out
 
@@ -637,7 +641,8 @@ def bench_rmsnorm(torch, gdn, steps, warmup) -> dict:
     log(f"gated rmsnorm 27B output: {ms * 1e3:.2f} us, {gbps:.0f} GB/s")
     return {"rows": rows, "D": D, "us_per_call": round(ms * 1e3, 3), "algorithmic_bytes": nbytes,
             "GBps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-            "timing": timing_summary(t)}
+            "timing": timing_summary(t),
+            "traffic": pmc_traffic(NORM_KERNEL, source_hash("conv_norm.hip", "gdn_device.h"))}
 
 
 def bench_decode(torch, gdn, d, steps, warmup, rotate: int = 1, clock=None):
@@ -808,10 +813,11 @@ def main():
                          "the checkpoint, raw-gate and multi-token legs would mix into the "
                          "same kernels' statistics)")
     ap.add_argument("--only", choices=["all", "prefill", "onchip", "decode", "decode_rot", "decode_B128",
-                                       "copy"],
+                                       "conv_norm", "copy"],
                     default="all",
                     help="restrict to one leg (profiling runs); 'copy' runs only the plain "
-                         "copy kernel used to calibrate HBM byte counters")
+                         "copy kernel used to calibrate HBM byte counters, 'conv_norm' the "
+                         "causal conv1d and gated RMS norm legs")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -952,7 +958,7 @@ def main():
         }
         log(f"long context: {ms_l:.3f} ms per prompt, {ms_l * 1e3 / ncalls:.1f} us per call")
 
-    if args.only in ("all", "prefill") and not args.no_extras:
+    if (args.only in ("all", "prefill") and not args.no_extras) or args.only == "conv_norm":
         # the operations around the recurrence, at the 27B layer's shapes
         result["conv1d"] = bench_conv1d(torch, gdn, steps, args.warmup)
         result["gated_rmsnorm"] = bench_rmsnorm(torch, gdn, steps, args.warmup)
