@@ -170,6 +170,20 @@ def test_gated_rmsnorm_matches_oracle(rows, D, dtype, gate):
     assert torch.equal(xd, y)
 
 
+@pytest.mark.parametrize("rows,D,dtype", [(77, 128, "bf16"), (5, 512, "bf16"), (10, 128, "f32")])
+def test_gated_rmsnorm_writes_nothing_past_the_rows(rows, D, dtype):
+    """The lanes past the last row of a ragged block (their stores dropped by
+    the buffer bound, not by a branch) leave the memory after y untouched."""
+    torch = torch_mod()
+    x, z, w = norm_case(rows, D, dtype, seed=3 * rows + D)
+    big = dev(np.full((rows + 64, D), 7.0, dtype=np.float32), dtype)
+    y = big[:rows]
+    gdn.gdn_gated_rmsnorm(dev(x, dtype), dev(z, dtype), dev32(w), 1e-6, out=y)
+    torch.cuda.synchronize()
+    assert torch.all(big[rows:] == 7.0)
+    close(host(y), oracle.gated_rmsnorm(x, z, w, eps=1e-6), dtype, f"rmsnorm {rows}x{D} into a larger buffer")
+
+
 def test_gated_rmsnorm_zero_rows_and_nan_isolation():
     torch = torch_mod()
     x, z, w = norm_case(16, 128, "bf16", seed=9)
