@@ -20,10 +20,13 @@
 //    here reads it again, and bypassing the caches gained ~7% (155 -> 145
 //    us).  The K-1 tokens before the tile come from the previous tile's rows
 //    (mostly cache hits) or, before the first token, from the carried state.
-//    A second small kernel, launched
-//    after it on the same stream, writes the new state (one thread per
-//    channel reads every old value it needs before writing, so the new state
-//    may overwrite the old one, also when T < K-1).
+//    The new state (one thread per 16 bytes of channels reads every old value
+//    it needs before writing, so it may overwrite the old one, also when
+//    T < K-1) is written by the conv kernel itself when a call is one tile per
+//    sequence (decode, short calls: 15.7 -> 13.2 us per call back to back at
+//    B=64, T=1 over the 27B channels), else by a second small kernel launched
+//    after it on the same
+//    stream, since then tile 0 reads the old state while the last tile ends.
 //  * gated RMS norm: a group of D/VEC lanes per row (two rows per group),
 //    the sum of squares reduced by shuffles in a fixed order; each lane reads
 //    its x and z before writing y, so y may be x.
@@ -83,12 +86,36 @@ __device__ __forceinline__ float silu(float x) {
     return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
 
-// grid: x = channel groups (C / N) in blocks of CONV_THREADS, y = token tiles,
-// z = sequences
+// new state [B, P, C] of sequence b at channels c0 .. c0 + 15 bytes: the last
+// P entries of concat(old state, x), copied bit for bit; every value is read
+// before any is written, so state_out may be state_in
 template <typename TIn, int K>
+__device__ __forceinline__ void carry_state(const TIn* x, const TIn* state_in, TIn* state_out, int T, int C,
+                                            int b, int c0) {
+    constexpr int P = K - 1;
+    uint4 keep[P > 0 ? P : 1];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int s = T - P + i;   // position in the sequence; < 0: from the old state
+        if (s >= 0)
+            keep[i] = *reinterpret_cast<const uint4*>(x + ((size_t)b * T + s) * C + c0);
+        else if (state_in)
+            keep[i] = *reinterpret_cast<const uint4*>(state_in + ((size_t)b * P + (P + s)) * C + c0);
+        else
+            keep[i] = uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+        *reinterpret_cast<uint4*>(state_out + ((size_t)b * P + i) * C + c0) = keep[i];
+}
+
+// grid: x = channel groups (C / N) in blocks of CONV_THREADS, y = token tiles,
+// z = sequences.  CARRY (one tile per sequence only): the thread also writes
+// the new state of its channels, which no other thread reads.
+template <typename TIn, int K, bool CARRY>
 __global__ __launch_bounds__(CONV_THREADS) void conv1d_kernel(
     const TIn* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
-    const TIn* __restrict__ state_in, TIn* __restrict__ y, int T, int C, int silu_on) {
+    const TIn* state_in, TIn* __restrict__ y, TIn* state_out, int T, int C, int silu_on) {
     constexpr int N = Vec16<TIn>::N;
     constexpr int P = K - 1;
     const int cg = blockIdx.x * CONV_THREADS + threadIdx.x;
@@ -161,33 +188,18 @@ __global__ __launch_bounds__(CONV_THREADS) void conv1d_kernel(
 #pragma unroll
     for (int r = 0; r < CONV_RING - 1; ++r)
         if (base + r < tn) step(ring[r], base + r);
+    if constexpr (CARRY) carry_state<TIn, K>(x, state_in, state_out, T, C, b, c0);
 }
 
-// new state [B, P, C]: the last P entries of concat(old state, x); one thread
-// per 16 bytes of channels, all reads before any write
+// new state [B, P, C] of every sequence (calls of more than one tile): one
+// thread per 16 bytes of channels, all reads before any write
 template <typename TIn, int K>
 __global__ __launch_bounds__(CONV_THREADS) void conv_state_kernel(
     const TIn* __restrict__ x, const TIn* state_in, TIn* state_out, int T, int C) {
     constexpr int N = Vec16<TIn>::N;
-    constexpr int P = K - 1;
     const int cg = blockIdx.x * CONV_THREADS + threadIdx.x;
     if (cg * N >= C) return;
-    const int c0 = cg * N;
-    const int b = blockIdx.y;
-    uint4 keep[P > 0 ? P : 1];
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-        const int s = T - P + i;   // position in the sequence; < 0: from the old state
-        if (s >= 0)
-            keep[i] = *reinterpret_cast<const uint4*>(x + ((size_t)b * T + s) * C + c0);
-        else if (state_in)
-            keep[i] = *reinterpret_cast<const uint4*>(state_in + ((size_t)b * P + (P + s)) * C + c0);
-        else
-            keep[i] = uint4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < P; ++i)
-        *reinterpret_cast<uint4*>(state_out + ((size_t)b * P + i) * C + c0) = keep[i];
+    carry_state<TIn, K>(x, state_in, state_out, T, C, blockIdx.y, cg * N);
 }
 
 template <typename TIn, int K>
@@ -195,13 +207,18 @@ hipError_t launch_conv_k(const ConvArgs& a, hipStream_t stream) {
     constexpr int N = Vec16<TIn>::N;
     const int groups = a.C / N;
     const TIn* x = static_cast<const TIn*>(a.x);
+    const TIn* st_in = static_cast<const TIn*>(a.state_in);
+    TIn* st_out = static_cast<TIn*>(a.state_out);
+    // one tile per sequence (decode, short calls): the conv kernel carries the
+    // state itself, one launch instead of two
+    const bool carry = st_out && K > 1 && a.T > 0 && a.T <= CONV_TT;
     if (a.B > 0 && a.T > 0) {
         const dim3 grid((groups + CONV_THREADS - 1) / CONV_THREADS, (a.T + CONV_TT - 1) / CONV_TT, a.B);
-        hipLaunchKernelGGL((conv1d_kernel<TIn, K>), grid, dim3(CONV_THREADS), 0, stream, x, a.w, a.bias,
-                           static_cast<const TIn*>(a.state_in), static_cast<TIn*>(a.y), a.T, a.C,
-                           a.silu);
+        const auto kern = carry ? conv1d_kernel<TIn, K, true> : conv1d_kernel<TIn, K, false>;
+        hipLaunchKernelGGL(kern, grid, dim3(CONV_THREADS), 0, stream, x, a.w, a.bias, st_in,
+                           static_cast<TIn*>(a.y), st_out, a.T, a.C, a.silu);
         const hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
+        if (err != hipSuccess || carry) return err;
     }
     if (a.state_out && a.B > 0 && K > 1) {
         const dim3 grid((groups + CONV_THREADS - 1) / CONV_THREADS, a.B);
