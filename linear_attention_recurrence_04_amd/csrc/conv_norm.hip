@@ -25,8 +25,8 @@
 //    T < K-1) is written by the conv kernel itself when a call is one tile per
 //    sequence (decode, short calls: 15.7 -> 13.2 us per call back to back at
 //    B=64, T=1 over the 27B channels), else by a second small kernel launched
-//    after it on the same
-//    stream, since then tile 0 reads the old state while the last tile ends.
+//    after it on the same stream, since then tile 0 reads the old state while
+//    the last tile ends.
 //  * gated RMS norm: a group of D/VEC lanes per row (two rows per group),
 //    the sum of squares reduced by shuffles in a fixed order; each lane reads
 //    its x and z before writing y, so y may be x.
