@@ -572,12 +572,23 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
 #pragma unroll
                     for (int ii = 0; ii < 2; ++ii) O4[ii] = mfma32(ap1[ii], DB1, O4[ii]);
                 }
+                // lane pairs (n, n ^ 1) trade two of their four rows, so each
+                // lane writes two rows of two adjacent columns as 4-byte words
 #pragma unroll
-                for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        Ot[16 * (2 * half + ii) + 4 * g + t][SW * st + n] =
-                            static_cast<uint16_t>(bfbits(q_scale * O4[ii][t]));
+                for (int ii = 0; ii < 2; ++ii) {
+                    const uint32_t lo = (uint32_t)(uint16_t)bfbits(q_scale * O4[ii][0]) |
+                                        ((uint32_t)(uint16_t)bfbits(q_scale * O4[ii][1]) << 16);
+                    const uint32_t hi = (uint32_t)(uint16_t)bfbits(q_scale * O4[ii][2]) |
+                                        ((uint32_t)(uint16_t)bfbits(q_scale * O4[ii][3]) << 16);
+                    const bool odd = (n & 1) != 0;
+                    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? lo : hi), 0xB1, 0xF, 0xF, false);
+                    const uint32_t pa = odd ? recv : lo;   // column n & ~1
+                    const uint32_t pb = odd ? hi : recv;   // column n | 1
+                    const int r0 = 16 * (2 * half + ii) + 4 * g + (odd ? 2 : 0);
+                    const int c0 = SW * st + (n & ~1);
+                    *reinterpret_cast<uint32_t*>(&Ot[r0][c0]) = (pa & 0xffffu) | (pb << 16);
+                    *reinterpret_cast<uint32_t*>(&Ot[r0 + 1][c0]) = (pa >> 16) | (pb & 0xffff0000u);
+                }
             }
             // ---- the wave's 32 rows x 64 bytes back from LDS (its own writes,
             //      so no barrier) and to HBM in 16-byte pieces
