@@ -109,6 +109,25 @@ def test_conv1d_split_invariance_and_in_place_state():
     assert torch.equal(torch.cat(outs, dim=1), y1) and torch.equal(state, s1)
 
 
+def test_conv1d_one_tile_and_multi_tile_calls_agree():
+    """A call of 200 tokens (four tiles: the state written by the separate
+    state kernel) against calls of 64, 1, 70 and 65 tokens (one tile: the conv
+    kernel writes the state itself; more: the state kernel), the state carried
+    in place: bitwise the same outputs and final state."""
+    torch = torch_mod()
+    x, st, w, b = conv_case(3, 200, 512, 4, "bf16", seed=6)
+    y1, s1 = run_conv(x, st, w, b, "bf16")
+    state = dev(st, "bf16")
+    xd, wd, bd = dev(x, "bf16"), dev32(w), dev32(b)
+    outs, t0 = [], 0
+    for n in (64, 1, 70, 65):
+        y, _ = gdn.gdn_causal_conv1d(xd[:, t0:t0 + n].contiguous(), wd, bd, state, state_out=state)
+        outs.append(y)
+        t0 += n
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs, dim=1), y1) and torch.equal(state, s1)
+
+
 def test_conv1d_decode_steps_in_place():
     """27B decode shape: 64 sequences, C = 10240 channels (q, k: 2 x 16 x 128;
     v: 48 x 128), 20 single-token calls updating the state in place, bitwise
