@@ -75,15 +75,29 @@ constexpr int SNT = 64 * (2 * NSTRIP + LWAVES);   // threads per workgroup
 constexpr int BVS = SW * NSTRIP;  // state columns per workgroup
 constexpr int OS = BVS + 8;       // row stride (elements) of the output staging tile
 
-// 16-byte chunk c of a 256-byte k or q row r is stored at c ^ swz(r).  Row
-// operand reads (16 rows, one chunk) and transposed reads (4 rows x 4 chunks
-// per 16 lanes) both hit 16 distinct chunk positions.
-__host__ __device__ constexpr int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// 16-byte chunk c of a 256-byte k or q row r is stored at c ^ swz(r).  The
+// LDS has 64 banks of 4 bytes, so a chunk's banks follow from its position in
+// the row.  A 16-byte read is served 16 lanes at a time, in the lane groups
+// {0-3, 12-15, 20-27} and {4-11, 16-19, 28-31} (and the same plus 32); an
+// 8-byte read, transposed or not, 32 lanes at a time (each half wave).
+// Row operand reads (lane 16g + n reads chunk 4ks + g of row 16i + n) are
+// conflict-free: swz maps rows {0-3, 12-15} onto chunk positions closed under
+// xor 1, and the partner lanes of a group differ in g by exactly that bit.
+// Transposed reads (half wave: rows 4g + j, j < 4, g < 2, x chunks 4A..4A+3,
+// one 8-byte half) reach only 16 bank pairs with 32 lanes, so two-way is their
+// floor; they meet it because swz(r) >> 2 takes each value twice over every
+// 8 consecutive rows.
+__host__ __device__ constexpr int swz(int r) { return (r & 1) | ((r & 8) >> 2) | ((r & 6) << 1); }
+// 16-byte chunk c of a 64-byte v row s (32 columns) is stored at c ^ vswz(s).
+// A transposed read of a strip's two chunks takes rows 4g + j of both g of a
+// half wave; vswz sends the rows of odd g to the other strip's chunk pair, so
+// that the 32 lanes reach 32 distinct bank pairs.
+__host__ __device__ constexpr int vswz(int s) { return ((s >> 3) & 1) | ((s >> 1) & 2); }
 
 struct KSet {              // state-wave inputs of one chunk
     uint4 K[C * 16];       // k rows, swizzled
     uint4 T[IMG_BYTES / 16];   // T image
-    uint4 V[C * 4];        // v rows of the 32 columns: chunk c of row s at c ^ ((s >> 2) & 3)
+    uint4 V[C * 4];        // v rows of the 32 columns: chunk c of row s at c ^ vswz(s)
     float gate[4 * C];     // grk, wrk, beta, Gamma_C
 };
 struct QSet {              // output-wave inputs of one chunk
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
 #pragma unroll
             for (int u = 0; u < NVB; ++u) {            // v: 4 blocks of 16 rows
                 const int s2 = 16 * (lw + LWAVES * u) + (lane >> 2);
-                offv[u] = 2u * (uint32_t)(min(s2, last) * rowv + 8 * ((lane & 3) ^ ((s2 >> 2) & 3)));
+                offv[u] = 2u * (uint32_t)(min(s2, last) * rowv + 8 * ((lane & 3) ^ vswz(s2)));
             }
         };
         const int last_rows = Tb - (NTb - 1) * C - 1;   // last row of the last chunk
@@ -386,7 +400,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                 auto ldkt = [&](int a, int kk) __attribute__((always_inline)) {
                     const int r0 = 32 * kk + 4 * g + (n >> 2);
                     const int ch = 4 * (a >> 1) + (n & 3);
-                    const int sz = ((n >> 2) << 2) | g;     // swz(r0) = swz(r0 + 16)
+                    const int sz = swz(4 * g + (n >> 2));   // = swz(r0) = swz(r0 + 16)
                     const s16x4 lo = ld_tr4(Kb + r0 * 256 + 16 * (ch ^ sz) + 8 * (a & 1));
                     const s16x4 hi = ld_tr4(Kb + (r0 + 16) * 256 + 16 * (ch ^ sz) + 8 * (a & 1));
                     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -408,7 +422,7 @@ __global__ __launch_bounds__(SNT) void chunk_scan_kernel(
                             // j = 0..3, at column 16 strip + n; it addresses row
                             // 16i + 4g + (n >> 2), columns 16 strip + 4 (n & 3) .. + 3
                             const int sr = 16 * i + 4 * g + (n >> 2);
-                            vt[i] = ld_tr4(Vb + sr * 64 + 16 * ((2 * strip + ((n >> 1) & 1)) ^ g) + 8 * (n & 1));
+                            vt[i] = ld_tr4(Vb + sr * 64 + 16 * ((2 * strip + ((n >> 1) & 1)) ^ vswz(sr)) + 8 * (n & 1));
                             grk[i] = *reinterpret_cast<const f32x4*>(&B.gate[0 * C + 16 * i + 4 * g]);
                         }
                     }
