@@ -24,7 +24,10 @@
  *    global state: a call enqueues kernels on the caller's stream only, so
  *    calls on different streams never wait on one another.  The one
  *    exception is gdn_chunk_prefill_noalloc, whose workspace is a fixed
- *    device array of the library (see there).
+ *    device array of the library (see there).  (The single-token decode
+ *    launcher asks the runtime once per process how many of its workgroups
+ *    fit on a compute unit and keeps that read-only figure; it sizes the
+ *    grid and couples no calls.)
  *  - Tensors are dense, row-major, innermost dimension last, exactly as listed;
  *    no strides.  Every pointer must be 16-byte aligned.
  *  - q, k, v and o share one storage dtype (gdn_problem.dtype).  log_g, beta
